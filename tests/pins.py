@@ -1,0 +1,445 @@
+"""Independent pins of the fp64 oracle.
+
+Each ``pin_*`` takes the implementation under test (so the mutation test can
+hand it a deliberately broken copy of the oracle) and raises AssertionError on
+a mismatch.  None of them re-types the oracle's formula: they compare against
+a different library routine (torch SDPA, torch softmax), closed forms,
+invariants the pages fix, or pure-Python brute force.
+
+Page references: [chathome] is news.chathome.org, "NVIDIA releases
+Nemotron-Labs-TwoTower ..." (inference, block-generation and evaluation
+paragraphs); [aiboss] is aiboss88.com, technical-principle section.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+TOL = 1e-12
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def rand_attn(rng, B, S, Hq, Hkv, D, lengths, std=1.0):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths)
+    T = int(off[-1])
+    return dict(
+        q=rng.standard_normal((B, S, Hq, D)) * std,
+        k_blk=rng.standard_normal((B, S, Hkv, D)) * std,
+        v_blk=rng.standard_normal((B, S, Hkv, D)),
+        k_ctx=rng.standard_normal((T, Hkv, D)) * std,
+        v_ctx=rng.standard_normal((T, Hkv, D)),
+        offsets=off,
+    )
+
+
+def call_attn(attn, a, scale=None):
+    return attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["offsets"], scale)
+
+
+def sdpa_seq(a, b, scale=None, causal=False, q_override=None):
+    """torch SDPA (CPU, float64, GQA) for sequence b over [context ; block]."""
+    lo, hi = int(a["offsets"][b]), int(a["offsets"][b + 1])
+    K = np.concatenate([a["k_ctx"][lo:hi], a["k_blk"][b]], axis=0)   # [N, Hkv, D]
+    V = np.concatenate([a["v_ctx"][lo:hi], a["v_blk"][b]], axis=0)
+    Q = a["q"][b] if q_override is None else q_override              # [M, Hq, D]
+    tq = torch.from_numpy(np.ascontiguousarray(Q.transpose(1, 0, 2)))[None]
+    tk = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, scale=scale, is_causal=causal, enable_gqa=True)
+    return o[0].numpy().transpose(1, 0, 2)                           # [M, Hq, D]
+
+
+def _close(x, y, tol=TOL, what=""):
+    err = float(np.max(np.abs(np.asarray(x) - np.asarray(y)))) if np.size(x) else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------------------
+# attention pins ([chathome] inference paragraph, [aiboss] technical principle)
+# ----------------------------------------------------------------------------
+def pin_attn_sdpa_general(attn):
+    """General ragged GQA case == torch SDPA on each sequence's [context ; block]."""
+    rng = np.random.default_rng(11)
+    for (B, S, Hq, Hkv, D, lens, scale) in [
+        (3, 5, 4, 2, 8, [0, 3, 7], None),
+        (2, 4, 6, 3, 16, [5, 1], 0.37),
+        (1, 3, 8, 1, 4, [9], None),
+        (2, 2, 4, 4, 8, [2, 0], None),
+    ]:
+        a = rand_attn(rng, B, S, Hq, Hkv, D, lens)
+        out = call_attn(attn, a, scale)
+        for b in range(B):
+            _close(out[b], sdpa_seq(a, b, scale), what=f"sdpa b={b} shape={(B, S, Hq, Hkv, D)}")
+
+
+def pin_attn_empty_context(attn):
+    """L_b = 0: plain bidirectional attention inside the block."""
+    rng = np.random.default_rng(12)
+    a = rand_attn(rng, 2, 6, 4, 2, 8, [0, 0])
+    out = call_attn(attn, a)
+    for b in range(2):
+        tq = torch.from_numpy(a["q"][b].transpose(1, 0, 2).copy())[None]
+        tk = torch.from_numpy(a["k_blk"][b].transpose(1, 0, 2).copy())[None]
+        tv = torch.from_numpy(a["v_blk"][b].transpose(1, 0, 2).copy())[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, enable_gqa=True)
+        _close(out[b], ref[0].numpy().transpose(1, 0, 2), what="empty context")
+
+
+def pin_attn_single_token_decode(attn):
+    """S = 1: the last row of causal attention over [context ; new token],
+    i.e. one autoregressive decode step over the cache ([chathome]
+    block-generation paragraph: AR commits one token per step)."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, D = 4, 2, 8
+    lens = [6, 0, 3]
+    a = rand_attn(rng, 3, 1, Hq, Hkv, D, lens)
+    out = call_attn(attn, a)
+    for b, L in enumerate(lens):
+        qfull = np.concatenate([rng.standard_normal((L, Hq, D)), a["q"][b]], axis=0)
+        ref = sdpa_seq(a, b, causal=True, q_override=qfull)
+        _close(out[b, 0], ref[-1], what=f"decode b={b}")
+
+
+def pin_attn_gqa_is_repeated_mha(attn):
+    """GQA equals multi-head attention on K/V heads repeated G times in order."""
+    rng = np.random.default_rng(14)
+    a = rand_attn(rng, 2, 3, 6, 2, 8, [4, 2])
+    G = 3
+    m = dict(a)
+    for k in ("k_blk", "v_blk"):
+        m[k] = np.repeat(a[k], G, axis=2)
+    for k in ("k_ctx", "v_ctx"):
+        m[k] = np.repeat(a[k], G, axis=1)
+    _close(call_attn(attn, a), call_attn(attn, m), what="gqa vs repeated mha")
+
+
+def pin_attn_uniform_keys(attn):
+    """All keys equal: every weight is 1/(L+S), output = mean of V."""
+    rng = np.random.default_rng(15)
+    a = rand_attn(rng, 2, 4, 4, 2, 8, [5, 3])
+    kvec = rng.standard_normal(8)
+    a["k_blk"][:] = kvec
+    a["k_ctx"][:] = kvec
+    out = call_attn(attn, a)
+    for b in range(2):
+        lo, hi = a["offsets"][b], a["offsets"][b + 1]
+        for h in range(4):
+            g = h // 2
+            V = np.concatenate([a["v_ctx"][lo:hi, g], a["v_blk"][b, :, g]], axis=0)
+            _close(out[b, :, h], np.broadcast_to(V.mean(axis=0), (4, 8)), what="uniform keys")
+
+
+def pin_attn_dominant_key(attn):
+    """One key scores >= 60 above all others: output = that key's V row."""
+    rng = np.random.default_rng(16)
+    B, S, Hq, Hkv, D = 1, 3, 2, 1, 4
+    a = rand_attn(rng, B, S, Hq, Hkv, D, [5], std=0.1)
+    a["q"][:] = 1.0
+    a["k_ctx"][3, 0, :] = 60.0          # score = 60*4/sqrt(4) = 120 vs |others| < 2
+    out = call_attn(attn, a)
+    _close(out[0], np.broadcast_to(a["v_ctx"][3, 0], (S, Hq, D)), tol=1e-12, what="dominant key")
+    a2 = rand_attn(rng, B, S, Hq, Hkv, D, [5], std=0.1)
+    a2["q"][:] = 1.0
+    a2["k_blk"][0, 2, 0, :] = 60.0      # a block key dominates
+    out2 = call_attn(attn, a2)
+    _close(out2[0], np.broadcast_to(a2["v_blk"][0, 2, 0], (S, Hq, D)), what="dominant block key")
+
+
+def pin_attn_permutation(attn):
+    """Permuting the block's tokens (Q, K, V together) permutes the outputs."""
+    rng = np.random.default_rng(17)
+    a = rand_attn(rng, 2, 6, 4, 2, 8, [3, 5])
+    perm = rng.permutation(6)
+    p = dict(a)
+    for k in ("q", "k_blk", "v_blk"):
+        p[k] = a[k][:, perm]
+    _close(call_attn(attn, p), call_attn(attn, a)[:, perm], what="permutation")
+
+
+def pin_attn_batch_independence(attn):
+    """Sequence b's output does not change when it is run alone."""
+    rng = np.random.default_rng(18)
+    a = rand_attn(rng, 3, 4, 4, 2, 8, [2, 0, 5])
+    out = call_attn(attn, a)
+    for b in range(3):
+        lo, hi = int(a["offsets"][b]), int(a["offsets"][b + 1])
+        one = dict(q=a["q"][b:b + 1], k_blk=a["k_blk"][b:b + 1], v_blk=a["v_blk"][b:b + 1],
+                   k_ctx=a["k_ctx"][lo:hi], v_ctx=a["v_ctx"][lo:hi],
+                   offsets=np.array([0, hi - lo]))
+        _close(call_attn(attn, one)[0], out[b], what=f"batch independence b={b}")
+
+
+def pin_attn_key_shift(attn):
+    """Adding one vector to every key of a KV head leaves the output unchanged."""
+    rng = np.random.default_rng(19)
+    a = rand_attn(rng, 2, 4, 4, 2, 8, [3, 6])
+    s = dict(a)
+    c = rng.standard_normal((2, 8))
+    s["k_blk"] = a["k_blk"] + c[None, None]
+    s["k_ctx"] = a["k_ctx"] + c[None]
+    _close(call_attn(attn, s), call_attn(attn, a), tol=1e-11, what="key shift")
+
+
+def pin_attn_linear_in_v(attn):
+    """O(alpha V1 + V2) = alpha O(V1) + O(V2)."""
+    rng = np.random.default_rng(20)
+    a1 = rand_attn(rng, 2, 3, 4, 2, 8, [4, 1])
+    a2 = dict(a1)
+    a2["v_blk"] = rng.standard_normal(a1["v_blk"].shape)
+    a2["v_ctx"] = rng.standard_normal(a1["v_ctx"].shape)
+    al = 2.5
+    a3 = dict(a1)
+    a3["v_blk"] = al * a1["v_blk"] + a2["v_blk"]
+    a3["v_ctx"] = al * a1["v_ctx"] + a2["v_ctx"]
+    _close(call_attn(attn, a3), al * call_attn(attn, a1) + call_attn(attn, a2), tol=1e-11,
+           what="linearity")
+
+
+def brute_attention(a, scale=None):
+    """Pure-Python loops, no numpy arithmetic."""
+    q, kb, vb, kc, vc, off = (a[k] for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx", "offsets"))
+    B, S, Hq, D = q.shape
+    Hkv = kb.shape[2]
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    out = [[[[0.0] * D for _ in range(Hq)] for _ in range(S)] for _ in range(B)]
+    for b in range(B):
+        keys, vals = [], []
+        for t in range(int(off[b]), int(off[b + 1])):
+            keys.append(t)
+        for h in range(Hq):
+            g = h // G
+            K = [[float(kc[t, g, d]) for d in range(D)] for t in keys] + \
+                [[float(kb[b, j, g, d]) for d in range(D)] for j in range(S)]
+            Vv = [[float(vc[t, g, d]) for d in range(D)] for t in keys] + \
+                 [[float(vb[b, j, g, d]) for d in range(D)] for j in range(S)]
+            for i in range(S):
+                sc_list = [sc * sum(float(q[b, i, h, d]) * k[d] for d in range(D)) for k in K]
+                mx = max(sc_list)
+                w = [math.exp(x - mx) for x in sc_list]
+                tot = sum(w)
+                for d in range(D):
+                    out[b][i][h][d] = sum(w[n] * Vv[n][d] for n in range(len(K))) / tot
+    return np.array(out)
+
+
+def pin_attn_brute_force(attn):
+    rng = np.random.default_rng(21)
+    for (B, S, Hq, Hkv, D, lens) in [(2, 3, 4, 2, 4, [2, 0]), (1, 2, 2, 1, 3, [4])]:
+        a = rand_attn(rng, B, S, Hq, Hkv, D, lens)
+        _close(call_attn(attn, a), brute_attention(a), what="brute force")
+        _close(call_attn(attn, a, 0.21), brute_attention(a, 0.21), what="brute force scaled")
+
+
+ATTN_PINS = [pin_attn_sdpa_general, pin_attn_empty_context, pin_attn_single_token_decode,
+             pin_attn_gqa_is_repeated_mha, pin_attn_uniform_keys, pin_attn_dominant_key,
+             pin_attn_permutation, pin_attn_batch_independence, pin_attn_key_shift,
+             pin_attn_linear_in_v, pin_attn_brute_force]
+
+
+# ----------------------------------------------------------------------------
+# commit pins ([chathome] block-generation and evaluation paragraphs)
+# ----------------------------------------------------------------------------
+def pin_conf_vs_torch(row_conf):
+    """p = max of torch.softmax (float64); token = torch.argmax (documented to
+    return the first maximal index)."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((3, 5, 50)) * 3
+    x[0, 1, 7] = x[0, 1, 30] = x[0, 1].max() + 1.0     # a tie: first index wins
+    p, tok = row_conf(x)
+    t = torch.from_numpy(x)
+    _close(p, torch.softmax(t, dim=-1).max(dim=-1).values.numpy(), what="p vs torch")
+    assert (np.asarray(tok) == torch.argmax(t, dim=-1).numpy()).all(), "token vs torch"
+    assert int(tok[0, 1]) == 7
+
+
+def pin_conf_closed_forms(row_conf):
+    V = 37
+    p, tok = row_conf(np.zeros((1, 1, V)))
+    _close(p, [[1.0 / V]], what="uniform row")
+    assert int(tok[0, 0]) == 0
+    for c, j in [(2.0, 5), (-1.5, 36), (9.0, 0)]:
+        x = np.zeros((1, 1, V))
+        x[0, 0, j] = c
+        p, tok = row_conf(x)
+        want = math.exp(c) / (math.exp(c) + V - 1) if c > 0 else 1.0 / (math.exp(c) + V - 1)
+        _close(p, [[want]], what=f"one-hot logit c={c}")
+        assert int(tok[0, 0]) == (j if c > 0 else (0 if j != 0 else 1))
+
+
+def pin_conf_large_logits(row_conf):
+    """Logits near 1e3 (exp overflows without the max shift) stay exact."""
+    x = np.full((1, 1, 4), 1000.0)
+    x[0, 0, 2] = 1000.0 + math.log(6.0)
+    p, tok = row_conf(x)
+    _close(p, [[6.0 / 9.0]], what="large logits")
+    assert int(tok[0, 0]) == 2
+
+
+def pin_commit_golden(commit):
+    """Hand-derived fixture (tests/golden/commit_closed_form.json)."""
+    with open(os.path.join(GOLDEN, "commit_closed_form.json")) as f:
+        g = json.load(f)
+    x = np.array(g["logits"], dtype=np.float64)
+    for case in g["cases"]:
+        r = commit(x, np.array(case["eligible"], dtype=np.uint8), case["gamma"])
+        assert np.asarray(r["commit"]).astype(int).tolist() == case["commit"], case["name"]
+        assert np.asarray(r["token"]).tolist() == g["token"], case["name"]
+        assert np.asarray(r["n_commit"]).tolist() == case["n_commit"], case["name"]
+        _close(r["maxprob"], np.array(g["maxprob"]), tol=1e-15, what=case["name"])
+
+
+def pin_commit_gamma_above_one(commit):
+    """gamma > 1: only the force-one rule commits -- exactly one eligible
+    position per sequence that has one, none otherwise."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((4, 6, 20)) * 2
+    el = (rng.random((4, 6)) < 0.6).astype(np.uint8)
+    el[3] = 0
+    r = commit(x, el, 1.5)
+    c = np.asarray(r["commit"]).astype(bool)
+    for b in range(4):
+        assert c[b].sum() == (1 if el[b].any() else 0)
+        assert not (c[b] & ~el[b].astype(bool)).any()
+    # AR-like loop: each step commits exactly one token (force-one only)
+
+
+def pin_commit_gamma_tiny(commit):
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((3, 5, 20))
+    el = (rng.random((3, 5)) < 0.7).astype(np.uint8)
+    r = commit(x, el, 1e-6)
+    assert (np.asarray(r["commit"]).astype(bool) == el.astype(bool)).all()
+
+
+def pin_commit_monotone(commit):
+    """Commit count is non-increasing as gamma rises, >= 1 when any position
+    is eligible, and ineligible positions never commit ([chathome]
+    evaluation paragraph: a lower gamma commits more tokens per step)."""
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((5, 8, 30)) * 2.5
+    el = (rng.random((5, 8)) < 0.8).astype(np.uint8)
+    el[0] = 1
+    prev = None
+    for gam in np.linspace(0.02, 1.2, 40):
+        r = commit(x, el, float(gam))
+        c = np.asarray(r["commit"]).astype(bool)
+        n = c.sum(axis=1)
+        assert not (c & ~el.astype(bool)).any()
+        assert ((n >= 1) | ~el.astype(bool).any(axis=1)).all()
+        if prev is not None:
+            assert (n <= prev).all()
+        prev = n
+
+
+def pin_commit_inclusive_threshold(commit):
+    """p == gamma exactly commits (V = 2, equal logits: p = 0.5 = gamma)."""
+    x = np.zeros((1, 2, 2))
+    x[0, 1] = [3.0, 0.0]         # p = 1/(1+e^-3) = 0.9526 also commits
+    r = commit(x, np.ones((1, 2), np.uint8), 0.5)
+    assert np.asarray(r["commit"]).astype(int).tolist() == [[1, 1]]
+    r = commit(x, np.ones((1, 2), np.uint8), 0.6)
+    assert np.asarray(r["commit"]).astype(int).tolist() == [[0, 1]]
+
+
+def pin_commit_float32_gamma(commit):
+    """gamma is the float32 value the kernel sees: float32(0.8) = 0.80000001192...,
+    so p = 0.8 + 5e-9 does not reach it, while p = 0.8 + 5e-8 does."""
+    def row(p):
+        return [math.log(p / (1.0 - p)), 0.0]
+    x = np.array([[row(0.9), row(0.8 + 5e-9), row(0.8 + 5e-8)]])
+    r = commit(x, np.ones((1, 3), np.uint8), 0.8)
+    assert np.asarray(r["commit"]).astype(int).tolist() == [[1, 0, 1]]
+
+
+def pin_commit_force_one_ties(commit):
+    """Force-one: largest p among ELIGIBLE positions, lowest position on ties."""
+    V = 10
+    x = np.zeros((2, 5, V))
+    # sequence 0: positions 1 and 3 tie at the eligible max; 4 is higher but ineligible
+    for i, c in [(0, 0.5), (1, 1.0), (2, 0.2), (3, 1.0), (4, 3.0)]:
+        x[0, i, 2] = c
+    el = np.array([[1, 1, 1, 1, 0], [0, 0, 1, 1, 1]], np.uint8)
+    x[1, 2, 0] = 0.7
+    x[1, 4, 0] = 0.7
+    r = commit(x, el, 0.99)
+    assert np.asarray(r["commit"]).astype(int).tolist() == [[0, 1, 0, 0, 0], [0, 0, 1, 0, 0]]
+
+
+COMMIT_PINS = [pin_commit_golden, pin_commit_gamma_above_one, pin_commit_gamma_tiny,
+               pin_commit_monotone, pin_commit_inclusive_threshold, pin_commit_float32_gamma,
+               pin_commit_force_one_ties]
+CONF_PINS = [pin_conf_vs_torch, pin_conf_closed_forms, pin_conf_large_logits]
+
+
+# ----------------------------------------------------------------------------
+# step / loop pins ([chathome] block-generation paragraph)
+# ----------------------------------------------------------------------------
+def _loop_logits(seed, B, S, V):
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal((B, S, V)) * 2 for _ in range(S + 2)]
+    return lambda t: xs[t]
+
+
+def pin_loop_force_one_is_ar(loop):
+    """With gamma > 1 only force-one commits: exactly one token per step and
+    exactly S steps per block -- the autoregressive one-token-per-step case."""
+    B, S = 3, 5
+    r = loop(_loop_logits(41, B, S, 12), B, S, 1.01)
+    assert r["steps"] == S and r["done"]
+    assert (np.asarray(r["commits_per_step"]) == 1).all()
+    assert (np.asarray(r["tokens"]) >= 0).all()
+
+
+def pin_loop_low_gamma_one_step(loop):
+    B, S = 2, 6
+    r = loop(_loop_logits(42, B, S, 12), B, S, 1e-9)
+    assert r["steps"] == 1 and r["done"]
+
+
+def pin_loop_steps_monotone(loop):
+    """Steps per block never rise as gamma falls, and every block finishes
+    within S steps."""
+    B, S = 4, 8
+    f = _loop_logits(43, B, S, 6)
+    prev = None
+    for gam in [0.1, 0.3, 0.5, 0.8, 0.95, 1.2]:
+        r = loop(f, B, S, gam)
+        assert r["done"] and r["steps"] <= S
+        st = np.asarray(r["steps_per_seq"])
+        if prev is not None:
+            assert (st >= prev).all()
+        prev = st
+
+
+def pin_step_masks(step):
+    """A step never re-masks a committed position, and changes the stored
+    token only where it commits."""
+    rng = np.random.default_rng(44)
+    a = rand_attn(rng, 2, 4, 4, 2, 8, [3, 2])
+    x = rng.standard_normal((2, 4, 9)) * 3
+    m_in = np.array([[1, 0, 1, 1], [0, 0, 1, 0]], np.uint8)
+    tok_in = np.array([[-1, 5, -1, -1], [2, 3, -1, 4]])
+    r = step(a, x, m_in, tok_in, 0.6)
+    mo = np.asarray(r["masked_out"]).astype(bool)
+    c = np.asarray(r["commit"]).astype(bool)
+    assert not (mo & ~m_in.astype(bool)).any()
+    assert (mo | c == m_in.astype(bool)).all() and not (mo & c).any()
+    t = np.asarray(r["tokens"])
+    assert (t[~c] == tok_in[~c]).all()
+    assert (t[c] == np.argmax(x, axis=-1)[c]).all()
+    assert r["n_masked_left"] == int(mo.sum())
+
+
+LOOP_PINS = [pin_loop_force_one_is_ar, pin_loop_low_gamma_one_step, pin_loop_steps_monotone]
+STEP_PINS = [pin_step_masks]

@@ -1,0 +1,30 @@
+"""The fp64 oracle against its independent pins (CPU)."""
+import pytest
+
+import oracle
+import pins
+
+
+@pytest.mark.parametrize("pin", pins.ATTN_PINS, ids=lambda f: f.__name__)
+def test_attention_pin(pin):
+    pin(oracle.block_attention)
+
+
+@pytest.mark.parametrize("pin", pins.CONF_PINS, ids=lambda f: f.__name__)
+def test_confidence_pin(pin):
+    pin(oracle.row_confidence)
+
+
+@pytest.mark.parametrize("pin", pins.COMMIT_PINS, ids=lambda f: f.__name__)
+def test_commit_pin(pin):
+    pin(oracle.confidence_commit)
+
+
+@pytest.mark.parametrize("pin", pins.LOOP_PINS, ids=lambda f: f.__name__)
+def test_loop_pin(pin):
+    pin(oracle.denoise_loop)
+
+
+@pytest.mark.parametrize("pin", pins.STEP_PINS, ids=lambda f: f.__name__)
+def test_step_pin(pin):
+    pin(oracle.denoise_step)

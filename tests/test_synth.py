@@ -1,0 +1,57 @@
+"""Seeded generators: determinism, shapes, and the bf16 storage cast."""
+import numpy as np
+import torch
+
+import synth
+
+
+def test_bf16_cast_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 37,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.0078125, 65504.0, -3.3e38, 1e-40],
+                                 np.float32)])
+    ours = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours == ref).all()
+    back = synth.bf16_bits_to_f32(ours)
+    assert (torch.from_numpy(back) == torch.from_numpy(x).to(torch.bfloat16).float()).all()
+
+
+def test_attention_inputs_deterministic_and_shaped():
+    w = synth.WORKLOADS["bf16_b64_ragged1k_8k"].with_(B=5, ctx_lo=10, ctx_hi=40)
+    a = synth.make_attention_inputs(w, 7)
+    b = synth.make_attention_inputs(w, 7)
+    for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx", "offsets"):
+        assert (a[k] == b[k]).all()
+    assert a["q"].shape == (5, 16, 32, 128) and a["q"].dtype == np.uint16
+    assert a["k_ctx"].shape == (a["total_ctx"], 2, 128)
+    assert a["offsets"][0] == 0 and (np.diff(a["offsets"]) == a["lengths"]).all()
+    assert ((a["lengths"] >= 10) & (a["lengths"] <= 40)).all()
+    c = synth.make_attention_inputs(w, 8)
+    assert not (a["q"] == c["q"]).all()
+
+
+def test_explicit_lengths_and_empty_context():
+    w = synth.WORKLOADS["tiny_f32_b1_ctx64"].with_(B=3)
+    a = synth.make_attention_inputs(w, 1, lengths=[0, 5, 0])
+    assert a["total_ctx"] == 5 and a["max_ctx"] == 5
+    assert a["q"].dtype == np.float32
+
+
+def test_peak_logit_model():
+    w = synth.WORKLOADS["bf16_b8_ctx4k"].with_(B=2, V=4096)
+    c = synth.make_commit_inputs(w, 3)
+    x = synth.bf16_bits_to_f32(c["logits"]).reshape(-1, w.V)
+    r = np.arange(x.shape[0])
+    assert (x[r, c["peak"]] == x.max(axis=1)).all()
+
+
+def test_loop_logits_peak_grows():
+    w = synth.WORKLOADS["bf16_b32_ctx2k_loop"].with_(B=2, V=512)
+    base, peak, stored = synth.loop_peak_values(w, 5, 4)
+    v = synth.bf16_bits_to_f32(stored)
+    assert (np.diff(v, axis=0) >= 0).all()
+    x2 = synth.loop_step_logits(base, peak, stored, 2)
+    assert (x2[np.arange(x2.shape[0]), peak] == stored[2]).all()
+    x0 = synth.loop_step_logits(base, peak, stored, 0)
+    assert (x0 == base).all()

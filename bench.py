@@ -1,0 +1,274 @@
+"""Denoise-step throughput on one MI355X.
+
+A step is one td_denoise_step: the block attention of one denoiser attention
+layer (64 blocks of S = 16 [MASK] positions over ragged cached contexts of
+1K..8K tokens, 32 query / 2 KV heads, head dim 128, bf16) plus the
+confidence-masked commit of the block's 131072-way logits at gamma = 0.8.
+Inputs are seeded synthetic data of that shape, resident in HBM before the
+timed region; several input sets rotate so that the 256 MB last-level cache
+cannot serve a step from the previous use of its data.
+
+Prints one JSON line (see the "metric" and "config" keys).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/sec (S=16, ctx 8K, B=64) and % of HBM/MFMA roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+ATTN_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_bf16_b64_ragged1k_8k.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, lengths):
+    """Bytes and flops the method itself must move / compute per step."""
+    e = 2 if w.dtype == "bf16" else 4
+    sum_l = int(lengths.sum())
+    attn_bytes = (sum_l * w.Hkv * w.D * 2 * e                       # context K and V
+                  + w.B * w.S * (w.Hq + 2 * w.Hkv) * w.D * e         # Q, block K and V
+                  + w.B * w.S * w.Hq * w.D * e)                      # out
+    attn_flops = 4 * w.Hq * w.S * w.D * (sum_l + w.B * w.S)
+    commit_bytes = w.B * w.S * w.V * e + w.B * w.S * 10
+    return attn_bytes, attn_flops, commit_bytes
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from committed rocprofv3
+    counter runs, valid only while the kernel source is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, a, c, el, budget_s):
+    """The fp64 oracle on a bounded sample of the same step: whole sequences
+    (attention of all heads + commit of all positions) until ``budget_s`` of
+    CPU time is spent, scaled to the full batch by context length (attention)
+    and by sequence count (commit)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f64 = synth.bf16_bits_to_f64
+    t_attn = t_commit = 0.0
+    keys = 0
+    n = 0
+    order = np.random.default_rng(0).permutation(w.B)
+    for b in order:
+        lo, hi = int(a["offsets"][b]), int(a["offsets"][b + 1])
+        t0 = time.perf_counter()
+        oracle.block_attention(f64(a["q"][b:b + 1]), f64(a["k_blk"][b:b + 1]), f64(a["v_blk"][b:b + 1]),
+                               f64(a["k_ctx"][lo:hi]), f64(a["v_ctx"][lo:hi]), np.array([0, hi - lo]))
+        t1 = time.perf_counter()
+        oracle.confidence_commit(f64(c["logits"][b:b + 1]), el[b:b + 1], w.gamma)
+        t2 = time.perf_counter()
+        t_attn += t1 - t0
+        t_commit += t2 - t1
+        keys += hi - lo + w.S
+        n += 1
+        if t_attn + t_commit >= budget_s:
+            break
+    total_keys = int(a["lengths"].sum()) + w.B * w.S
+    step_s = t_attn * total_keys / keys + t_commit * w.B / n
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {w.B} sequences (attention of all 32 heads + commit of all "
+                      f"{w.S} positions), {t_attn + t_commit:.1f} s of fp64 numpy; scaled to the "
+                      f"batch by context keys (attention) and sequence count (commit)",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16_b64_ragged1k_8k")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1.5 GB total)")
+    ap.add_argument("--seed", type=int, default=1003)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the denoise step of one attention layer is one "
+              "GPU's share (sequences shard over GPUs with no exchange); --gpus above 1 is not "
+              "supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_lm_td_amd as td
+    from block_diffusion_lm_td_amd import _td
+    import synth
+
+    L = td.lib()
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name}")
+    a = synth.make_attention_inputs(w, args.seed)
+    c = synth.make_commit_inputs(w, args.seed)
+    el = np.ones((w.B, w.S), np.uint8)             # a fresh block: every position [MASK]
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    base = {k: up(a[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx")}
+    base["logits"] = up(c["logits"])
+    off = torch.from_numpy(a["offsets"]).to(dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = args.sets or max(2, int(np.ceil(1.5e9 / set_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    B, S = w.B, w.S
+    outs = []
+    structs = []
+    for st in sets:
+        o = dict(out=torch.empty_like(st["q"]),
+                 commit=torch.empty((B, S), dtype=torch.uint8, device=dev),
+                 token=torch.empty((B, S), dtype=torch.int32, device=dev),
+                 maxprob=torch.empty((B, S), dtype=torch.float32, device=dev),
+                 n_commit=torch.empty((B,), dtype=torch.int32, device=dev),
+                 masked_in=torch.from_numpy(el).to(dev),
+                 masked_out=torch.empty((B, S), dtype=torch.uint8, device=dev),
+                 tokens=torch.full((B, S), -1, dtype=torch.int32, device=dev),
+                 n_left=torch.empty((1,), dtype=torch.int32, device=dev))
+        aa = td.attn_args(st["q"], st["k_blk"], st["v_blk"], st["k_ctx"], st["v_ctx"], off, o["out"],
+                          a["total_ctx"], a["max_ctx"])
+        cc = td.commit_args(st["logits"], o["commit"], o["token"], w.gamma, o["masked_in"],
+                            o["maxprob"], o["n_commit"], o["masked_out"], o["tokens"], o["n_left"])
+        outs.append(o)
+        structs.append((aa, cc))
+    ws_bytes = max(L.td_denoise_workspace_bytes(ctypes.byref(aa), ctypes.byref(cc)) for aa, cc in structs)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    refs = [(ctypes.byref(aa), ctypes.byref(cc)) for aa, cc in structs]
+    log(f"[bench] {nsets} input sets x {set_bytes / 1e6:.0f} MB, workspace {ws_bytes / 1e6:.1f} MB")
+
+    def step(i):
+        ra, rc = refs[i % nsets]
+        r = L.td_denoise_step(ra, rc, ws_ptr, ws.numel(), sp)
+        if r != 0:
+            raise RuntimeError(_td.status_str(r))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    log(f"[bench] {args.steps} steps in {total_ms:.3f} ms -> {ms_per_step * 1e3:.1f} us/step")
+
+    # ---- per-kernel durations: HIP events around each part on the launch stream
+    ra_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    for i in range(args.steps):
+        aa_ref, cc_ref = refs[i % nsets]
+        ra_ev[3 * i].record(stream)
+        r1 = L.td_block_attn(aa_ref, ws_ptr, ws.numel(), sp)
+        ra_ev[3 * i + 1].record(stream)
+        r2 = L.td_commit(cc_ref, ws_ptr, ws.numel(), sp)
+        ra_ev[3 * i + 2].record(stream)
+        if r1 or r2:
+            raise RuntimeError(_td.status_str(r1 or r2))
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([ra_ev[3 * i].elapsed_time(ra_ev[3 * i + 1]) for i in range(args.steps)]))
+    commit_ms = float(np.mean([ra_ev[3 * i + 1].elapsed_time(ra_ev[3 * i + 2]) for i in range(args.steps)]))
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- committed tokens per step (every set holds the same data)
+    step(0)
+    torch.cuda.synchronize()
+    committed = int(outs[0]["n_commit"].sum().item())
+
+    attn_bytes, attn_flops, commit_bytes = algorithmic(w, a["lengths"])
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    steps_per_s = 1e3 / ms_per_step
+    res = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "S": S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "ctx_len": f"uniform integer in [{w.ctx_lo}, {w.ctx_hi}]" if w.ctx_lo != w.ctx_hi
+                   else w.ctx_lo, "total_ctx": int(a["total_ctx"]), "V": w.V, "gamma": w.gamma,
+                   "input_sets": nsets},
+        "tokens_per_s": round(committed * steps_per_s, 1),
+        "committed_per_step": committed,
+        "roofline": {"bound": "hbm", "kernel": "td_block_attn (attn_bf16_mfma + attn_combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": attn_bytes, "avg_launch_us": round(attn_ms * 1e3, 2),
+                     "mfma_tflops": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(attn_flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "commit": {"avg_launch_us": round(commit_ms * 1e3, 2), "algorithmic_bytes": commit_bytes,
+                   "achieved_GBs": round(commit_bytes / (commit_ms * 1e-3) / 1e9, 1)},
+        "step_roofline_frac": round((attn_bytes + commit_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(w, a, c, el, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""Block-diffusion denoise step (TwoTower denoiser attention + confidence
+commit) on AMD MI355X: a thin Python binding of libtd.so (include/td.h)."""
+from ._td import (  # noqa: F401
+    TD_BF16,
+    TD_F32,
+    TD_OK,
+    TdAttnArgs,
+    TdCommitArgs,
+    Workspace,
+    attn_args,
+    commit_args,
+    header_functions,
+    lib,
+    status_str,
+    td_block_attn,
+    td_commit,
+    td_denoise_step,
+)

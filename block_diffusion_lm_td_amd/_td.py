@@ -1,0 +1,224 @@
+"""ctypes binding of libtd.so (include/td.h).
+
+Argument marshalling only: torch tensors supply device pointers and the HIP
+stream, every step of the computation runs in the library's kernels.  There
+is no fallback: if libtd.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtd.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "td.h")
+
+TD_OK, TD_ERR_INVALID, TD_ERR_UNSUPPORTED, TD_ERR_WORKSPACE, TD_ERR_HIP = 0, -1, -2, -3, -4
+TD_F32, TD_BF16 = 0, 1
+
+
+class TdAttnArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("D", c_int32), ("dtype", c_int), ("scale", c_float),
+                ("q", c_void_p), ("k_blk", c_void_p), ("v_blk", c_void_p),
+                ("k_ctx", c_void_p), ("v_ctx", c_void_p), ("ctx_offsets", c_void_p),
+                ("total_ctx", c_int64), ("max_ctx", c_int64), ("out", c_void_p)]
+
+
+class TdCommitArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("V", c_int32), ("dtype", c_int),
+                ("gamma", c_float), ("logits", c_void_p), ("masked_in", c_void_p),
+                ("commit", c_void_p), ("token", c_void_p), ("maxprob", c_void_p),
+                ("n_commit", c_void_p), ("masked_out", c_void_p), ("tokens", c_void_p),
+                ("n_masked_left", c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtd.so once; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_diffusion_lm_td_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        A, C = ctypes.POINTER(TdAttnArgs), ctypes.POINTER(TdCommitArgs)
+        sig = {
+            "td_abi_version": (c_uint32, []),
+            "td_sizeof_attn_args": (c_size_t, []),
+            "td_sizeof_commit_args": (c_size_t, []),
+            "td_status_str": (ctypes.c_char_p, [c_int]),
+            "td_attn_workspace_bytes": (c_size_t, [A]),
+            "td_commit_workspace_bytes": (c_size_t, [C]),
+            "td_denoise_workspace_bytes": (c_size_t, [A, C]),
+            "td_block_attn": (c_int, [A, c_void_p, c_size_t, c_void_p]),
+            "td_commit": (c_int, [C, c_void_p, c_size_t, c_void_p]),
+            "td_denoise_step": (c_int, [A, C, c_void_p, c_size_t, c_void_p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        if L.td_sizeof_attn_args() != ctypes.sizeof(TdAttnArgs) or \
+                L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs):
+            raise RuntimeError("libtd.so struct layout does not match the binding")
+        _lib = L
+    return _lib
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions include/td.h declares."""
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(td_\w+)\s*\(", txt)))
+
+
+def status_str(rc: int) -> str:
+    return lib().td_status_str(rc).decode()
+
+
+def check(rc: int, what: str) -> None:
+    if rc != TD_OK:
+        raise RuntimeError(f"{what}: {status_str(rc)}")
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TD_BF16
+    if t.dtype == torch.float32:
+        return TD_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+def attn_args(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, total_ctx, max_ctx,
+              scale=0.0) -> TdAttnArgs:
+    torch = _torch()
+    B, S, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    dt = q.dtype
+    a = TdAttnArgs()
+    a.B, a.S, a.Hq, a.Hkv, a.D = B, S, Hq, Hkv, D
+    a.dtype = _dtype_code(q)
+    a.scale = float(scale)
+    a.q = _ptr(q, "q", dt)
+    a.k_blk = _ptr(k_blk, "k_blk", dt, (B, S, Hkv, D))
+    a.v_blk = _ptr(v_blk, "v_blk", dt, (B, S, Hkv, D))
+    a.k_ctx = _ptr(k_ctx, "k_ctx", dt, (total_ctx, Hkv, D))
+    a.v_ctx = _ptr(v_ctx, "v_ctx", dt, (total_ctx, Hkv, D))
+    a.ctx_offsets = _ptr(ctx_offsets, "ctx_offsets", torch.int64, (B + 1,))
+    a.total_ctx, a.max_ctx = int(total_ctx), int(max_ctx)
+    a.out = _ptr(out, "out", dt, (B, S, Hq, D))
+    return a
+
+
+def commit_args(logits, commit, token, gamma, masked_in=None, maxprob=None, n_commit=None,
+                masked_out=None, tokens=None, n_masked_left=None) -> TdCommitArgs:
+    torch = _torch()
+    B, S, V = logits.shape
+    c = TdCommitArgs()
+    c.B, c.S, c.V = B, S, V
+    c.dtype = _dtype_code(logits)
+    c.gamma = float(gamma)
+    c.logits = _ptr(logits, "logits")
+    c.masked_in = _ptr(masked_in, "masked_in", torch.uint8, (B, S))
+    c.commit = _ptr(commit, "commit", torch.uint8, (B, S))
+    c.token = _ptr(token, "token", torch.int32, (B, S))
+    c.maxprob = _ptr(maxprob, "maxprob", torch.float32, (B, S))
+    c.n_commit = _ptr(n_commit, "n_commit", torch.int32, (B,))
+    c.masked_out = _ptr(masked_out, "masked_out", torch.uint8, (B, S))
+    c.tokens = _ptr(tokens, "tokens", torch.int32, (B, S))
+    c.n_masked_left = _ptr(n_masked_left, "n_masked_left", torch.int32, (1,))
+    return c
+
+
+class Workspace:
+    """Caller-owned device scratch for the td_* calls (a torch byte tensor,
+    grown on demand; torch's allocator returns 256-byte aligned blocks)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        return c_void_p(self.buf.data_ptr()), self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _ws(workspace, device):
+    if workspace is not None:
+        return workspace
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def td_block_attn(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, *, total_ctx, max_ctx,
+                  scale=0.0, workspace=None, stream=None):
+    L = lib()
+    a = attn_args(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, total_ctx, max_ctx, scale)
+    need = L.td_attn_workspace_bytes(ctypes.byref(a))
+    ptr, n = _ws(workspace, q.device).get(need)
+    check(L.td_block_attn(ctypes.byref(a), ptr, n, _stream(stream)), "td_block_attn")
+    return out
+
+
+def td_commit(logits, commit, token, *, gamma, masked_in=None, maxprob=None, n_commit=None,
+              masked_out=None, tokens=None, n_masked_left=None, workspace=None, stream=None):
+    L = lib()
+    c = commit_args(logits, commit, token, gamma, masked_in, maxprob, n_commit, masked_out,
+                    tokens, n_masked_left)
+    need = L.td_commit_workspace_bytes(ctypes.byref(c))
+    ptr, n = _ws(workspace, logits.device).get(need)
+    check(L.td_commit(ctypes.byref(c), ptr, n, _stream(stream)), "td_commit")
+
+
+def td_denoise_step(attn: TdAttnArgs, commit: TdCommitArgs, *, workspace=None, device=None,
+                    stream=None):
+    """One denoise step from prepared argument structs (see attn_args /
+    commit_args): block attention, then the commit, on one stream."""
+    L = lib()
+    need = L.td_denoise_workspace_bytes(ctypes.byref(attn), ctypes.byref(commit))
+    ptr, n = _ws(workspace, device).get(need)
+    check(L.td_denoise_step(ctypes.byref(attn), ctypes.byref(commit), ptr, n, _stream(stream)),
+          "td_denoise_step")

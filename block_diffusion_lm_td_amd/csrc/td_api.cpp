@@ -1,0 +1,87 @@
+// extern "C" entry points of libtd.so (declared and documented in td.h).
+// Validation and planning happen here, on the host, before anything is
+// enqueued; the launchers live in td_attn.hip / td_commit.hip.
+#include <stdint.h>
+
+#include "td_internal.h"
+
+using namespace td;
+
+namespace {
+
+int check_ws(size_t need, void *ws, size_t ws_bytes) {
+  if (need == 0) return TD_OK;
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return TD_ERR_WORKSPACE;
+  return TD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t td_abi_version(void) { return TD_ABI_VERSION; }
+size_t td_sizeof_attn_args(void) { return sizeof(td_attn_args); }
+size_t td_sizeof_commit_args(void) { return sizeof(td_commit_args); }
+
+const char *td_status_str(int status) {
+  switch (status) {
+    case TD_OK: return "TD_OK";
+    case TD_ERR_INVALID: return "TD_ERR_INVALID: invalid argument";
+    case TD_ERR_UNSUPPORTED: return "TD_ERR_UNSUPPORTED: valid but unsupported configuration";
+    case TD_ERR_WORKSPACE: return "TD_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case TD_ERR_HIP: return "TD_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown td_status";
+  }
+}
+
+size_t td_attn_workspace_bytes(const td_attn_args *a) {
+  if (validate_attn(a, false) != TD_OK) return 0;
+  return plan_attn(a).ws_bytes;
+}
+
+size_t td_commit_workspace_bytes(const td_commit_args *c) {
+  if (validate_commit(c, false) != TD_OK) return 0;
+  return plan_commit(c).ws_bytes;
+}
+
+size_t td_denoise_workspace_bytes(const td_attn_args *a, const td_commit_args *c) {
+  if (validate_attn(a, false) != TD_OK || validate_commit(c, false) != TD_OK) return 0;
+  return align256(plan_attn(a).ws_bytes) + align256(plan_commit(c).ws_bytes);
+}
+
+int td_block_attn(const td_attn_args *a, void *ws, size_t ws_bytes, td_stream_t stream) {
+  int rc = validate_attn(a, true);
+  if (rc != TD_OK) return rc;
+  const AttnPlan p = plan_attn(a);
+  rc = check_ws(p.ws_bytes, ws, ws_bytes);
+  if (rc != TD_OK) return rc;
+  return launch_attn(a, p, ws, stream);
+}
+
+int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t stream) {
+  int rc = validate_commit(c, true);
+  if (rc != TD_OK) return rc;
+  const CommitPlan p = plan_commit(c);
+  rc = check_ws(p.ws_bytes, ws, ws_bytes);
+  if (rc != TD_OK) return rc;
+  return launch_commit(c, p, ws, stream);
+}
+
+int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws, size_t ws_bytes,
+                    td_stream_t stream) {
+  int rc = validate_attn(a, true);
+  if (rc != TD_OK) return rc;
+  rc = validate_commit(c, true);
+  if (rc != TD_OK) return rc;
+  if (a->B != c->B || a->S != c->S) return TD_ERR_INVALID;
+  const AttnPlan pa = plan_attn(a);
+  const CommitPlan pc = plan_commit(c);
+  const size_t wa = align256(pa.ws_bytes), wc = align256(pc.ws_bytes);
+  rc = check_ws(wa + wc, ws, ws_bytes);
+  if (rc != TD_OK) return rc;
+  rc = launch_attn(a, pa, ws, stream);
+  if (rc != TD_OK) return rc;
+  return launch_commit(c, pc, static_cast<char *>(ws) + wa, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal declarations shared by the host library's translation units.
+// Not part of the public ABI (include/td.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "td.h"
+
+namespace td {
+
+// Tiling constants of the bf16 MFMA attention kernel.
+constexpr int kRowsPerWG = 256;   // query rows (G*S rows of one KV head) per workgroup
+constexpr int kKeyTile = 32;      // keys per LDS tile
+constexpr int kWGThreads = 256;   // 4 waves of 64
+
+// Launch plan of one td_block_attn call, derived on the host from sizes only.
+struct AttnPlan {
+  bool mfma;            // bf16, D == 128: MFMA kernel; otherwise the VALU kernel
+  int G;                // Hq / Hkv
+  int M;                // G * S query rows per (b, kv head)
+  int row_groups;       // ceil(M / kRowsPerWG)   (MFMA path)
+  int chunk;            // keys per split (multiple of kKeyTile)      (MFMA path)
+  int nchunks;          // ceil((max_ctx + S) / chunk)                (MFMA path)
+  int64_t units;        // B * Hkv * row_groups
+  size_t ws_o_bytes;    // partial O, fp32, per (unit, chunk)
+  size_t ws_ml_bytes;   // partial (m, l) per (unit, chunk, row)
+  size_t ws_bytes;      // total, 256-byte aligned pieces
+  float scale_log2;     // scale * log2(e)
+};
+
+struct CommitPlan {
+  int R;                // workgroups per row
+  int span;             // elements per workgroup (multiple of the vector width)
+  bool vec;             // 16-byte vector loads usable
+  int64_t rows;         // B * S
+  size_t ws_bytes;
+};
+
+// Host-side validation and planning (td_plan.cpp): pure functions.
+int validate_attn(const td_attn_args *a, bool check_ptrs);
+int validate_commit(const td_commit_args *c, bool check_ptrs);
+AttnPlan plan_attn(const td_attn_args *a);
+CommitPlan plan_commit(const td_commit_args *c);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Launchers (td_attn.hip / td_commit.hip); return a td_status.
+int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream);
+int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream);
+
+}  // namespace td

@@ -1,0 +1,156 @@
+/*
+ * td.h -- C ABI of the block-diffusion denoise step for AMD MI355X (gfx950).
+ *
+ * One denoising step of the TwoTower diffusion denoiser, as described on the
+ * news pages about NVIDIA's Nemotron-Labs-TwoTower:
+ *   - news.chathome.org, "NVIDIA releases Nemotron-Labs-TwoTower: an
+ *     open-weight diffusion language model built on a frozen autoregressive
+ *     backbone": inference paragraph (the denoiser attends bidirectionally
+ *     inside its block and, layer by layer, to the context tower's per-layer
+ *     KV cache of the prompt and committed tokens); block-generation
+ *     paragraph (a block of S [MASK] tokens is refined step by step and
+ *     several tokens may commit per step); evaluation paragraph (confidence
+ *     masking with threshold gamma = 0.8, block size S = 16).
+ *   - aiboss88.com, "Nemotron-Labs-TwoTower", technical-principle section
+ *     (bidirectional block attention plus cross-attention to the context
+ *     tower).
+ *
+ * Conventions shared by every entry point
+ *   Memory     Every data pointer is DEVICE memory owned by the caller.  The
+ *              library never allocates, frees or keeps a pointer after a call
+ *              returns; scratch space is the caller's workspace, sized by the
+ *              *_workspace_bytes queries.  The library keeps no mutable
+ *              global state, so calls on different streams may run at once
+ *              as long as they use different workspaces.
+ *   Streams    Work is enqueued in order on the caller's stream (a
+ *              hipStream_t passed as td_stream_t; NULL = the null stream).
+ *              The library never synchronises; outputs are valid once the
+ *              stream has executed the work.
+ *   Errors     All arguments are checked on the host before anything is
+ *              enqueued: a non-zero return means nothing was enqueued and no
+ *              output was written.  TD_ERR_HIP reports a launch failure seen
+ *              right after enqueueing (outputs then undefined).  The device
+ *              offsets array cannot be checked on the host; the kernels
+ *              clamp every row index to [0, total_ctx), so inconsistent
+ *              offsets give unspecified values but never an out-of-bounds
+ *              access.
+ *   Layouts    Row-major, innermost index last, no padding.
+ *   Results    Deterministic: the same inputs give bitwise-identical outputs
+ *              (no floating-point atomics; partials merged in a fixed order).
+ */
+#ifndef TD_H
+#define TD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TD_ABI_VERSION 1u
+
+typedef enum {
+  TD_OK = 0,
+  TD_ERR_INVALID = -1,      /* a null pointer, a bad size or a bad value    */
+  TD_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. D = 96)      */
+  TD_ERR_WORKSPACE = -3,    /* ws too small or misaligned (256 B required)  */
+  TD_ERR_HIP = -4           /* the HIP runtime reported a launch failure    */
+} td_status;
+
+typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
+
+typedef void *td_stream_t;  /* a hipStream_t */
+
+/*
+ * Block attention of one denoiser attention layer (chathome, inference
+ * paragraph; aiboss, technical principle).  For sequence b and query head h,
+ * with KV head g = h / (Hq/Hkv):
+ *   K = [k_ctx rows off[b] .. off[b+1]-1, head g ; k_blk[b, 0..S-1, g]]
+ *   V = the same rows of v_ctx / v_blk
+ *   out[b, :, h] = softmax(scale * q[b, :, h] K^T over all L_b + S keys) V
+ * One softmax covers the cached context and the block: bidirectional inside
+ * the block, every cached key visible, no mask.
+ */
+typedef struct {
+  int32_t B;               /* sequences (blocks) in the batch, >= 1            */
+  int32_t S;               /* block size, 1 .. 64                              */
+  int32_t Hq, Hkv;         /* query / KV heads, Hq % Hkv == 0, Hq/Hkv <= 64    */
+  int32_t D;               /* head dim: 64 or 128 (bf16 requires 128)          */
+  td_dtype dtype;          /* dtype of q, k_*, v_*, out (one per call)         */
+  float scale;             /* softmax scale; <= 0 selects 1/sqrt(D)            */
+  const void *q;           /* [B, S, Hq, D]                                    */
+  const void *k_blk;       /* [B, S, Hkv, D]  block keys                       */
+  const void *v_blk;       /* [B, S, Hkv, D]  block values                     */
+  const void *k_ctx;       /* [total_ctx, Hkv, D] context keys, packed per seq */
+  const void *v_ctx;       /* [total_ctx, Hkv, D] context values               */
+  const int64_t *ctx_offsets; /* DEVICE [B+1]: off[0] = 0, non-decreasing,
+                                 off[B] = total_ctx; L_b = off[b+1]-off[b] >= 0 */
+  int64_t total_ctx;       /* HOST copy of off[B]                              */
+  int64_t max_ctx;         /* HOST copy of max_b L_b (sizes the launch grid)   */
+  void *out;               /* [B, S, Hq, D], dtype as q; may not alias inputs  */
+} td_attn_args;
+
+/*
+ * Confidence-masked commit of one block step (chathome, evaluation and
+ * block-generation paragraphs).  For every position (b, i):
+ *   token[b,i]   = lowest id j with logits[b,i,j] == max_j logits[b,i,j]
+ *   maxprob[b,i] = 1 / sum_j exp(logits[b,i,j] - max)   (largest softmax prob.)
+ * Per sequence b, with E = {i : masked_in[b,i] != 0}:
+ *   C = {i in E : maxprob[b,i] >= gamma};  if C is empty and E is not,
+ *   C = {the i in E with the largest maxprob, lowest i on ties}.
+ *   commit[b,i] = (i in C); n_commit[b] = |C|
+ *   masked_out[b,i] = masked_in[b,i] && !commit[b,i]
+ *   tokens[b,i] = token[b,i] where commit[b,i], unchanged elsewhere
+ *   *n_masked_left = number of nonzero masked_out over the whole batch
+ * maxprob is computed in fp32 (relative error ~1e-6); gamma is compared as
+ * the fp32 value given.
+ */
+typedef struct {
+  int32_t B;               /* >= 1                                             */
+  int32_t S;               /* 1 .. 64                                          */
+  int32_t V;               /* vocabulary size, >= 1                            */
+  td_dtype dtype;          /* dtype of logits                                  */
+  float gamma;             /* confidence threshold, finite                     */
+  const void *logits;      /* [B, S, V]                                        */
+  const uint8_t *masked_in;/* [B, S] 1 = still [MASK] (eligible); NULL = all   */
+  uint8_t *commit;         /* out [B, S]  1 = committed by this step           */
+  int32_t *token;          /* out [B, S]  argmax id at EVERY position          */
+  float *maxprob;          /* out [B, S] or NULL                               */
+  int32_t *n_commit;       /* out [B] or NULL                                  */
+  uint8_t *masked_out;     /* out [B, S] or NULL; may alias masked_in          */
+  int32_t *tokens;         /* in/out [B, S] or NULL: ids written where committed */
+  int32_t *n_masked_left;  /* out [1] or NULL                                  */
+} td_commit_args;
+
+/* Library identity and struct sizes, for bindings to check their layout. */
+uint32_t td_abi_version(void);
+size_t td_sizeof_attn_args(void);
+size_t td_sizeof_commit_args(void);
+const char *td_status_str(int status);
+
+/* Workspace each call needs, in bytes (0 when none).  Pure host functions:
+ * they validate the arguments' sizes (not pointers) and return 0 on invalid
+ * sizes; pass a workspace of at least this many bytes, 256-byte aligned. */
+size_t td_attn_workspace_bytes(const td_attn_args *a);
+size_t td_commit_workspace_bytes(const td_commit_args *c);
+size_t td_denoise_workspace_bytes(const td_attn_args *a, const td_commit_args *c);
+
+/* Block attention (see td_attn_args).  Returns a td_status. */
+int td_block_attn(const td_attn_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* Confidence-masked commit (see td_commit_args).  Returns a td_status. */
+int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* One denoise step: the block attention of one denoiser attention layer and
+ * the commit of the block's logits, both enqueued on `stream`.  The logits
+ * are an input: the layers between this attention and the LM head are not
+ * part of this library.  a->B must equal c->B and a->S must equal c->S.
+ * One workspace of td_denoise_workspace_bytes() serves both parts. */
+int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws,
+                    size_t ws_bytes, td_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TD_H */

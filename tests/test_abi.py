@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: libtd.so loads, exports every function
+include/td.h declares, its structs match the binding, and invalid arguments
+are rejected on the host before anything is enqueued (no compute calls)."""
+import ctypes
+
+import pytest
+
+import block_diffusion_lm_td_amd as td
+from block_diffusion_lm_td_amd import _td
+
+INVALID, UNSUPPORTED, WORKSPACE = _td.TD_ERR_INVALID, _td.TD_ERR_UNSUPPORTED, _td.TD_ERR_WORKSPACE
+FAKE = 0x10000          # a non-null pointer value; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    return td.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = _td.header_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(_td.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"libtd.so does not export {n}"
+
+
+def test_struct_layout_and_version(L):
+    assert L.td_abi_version() == 1
+    assert L.td_sizeof_attn_args() == ctypes.sizeof(_td.TdAttnArgs)
+    assert L.td_sizeof_commit_args() == ctypes.sizeof(_td.TdCommitArgs)
+    for rc in (0, -1, -2, -3, -4, 7):
+        assert isinstance(td.status_str(rc), str)
+
+
+def attn(**kw):
+    a = _td.TdAttnArgs()
+    a.B, a.S, a.Hq, a.Hkv, a.D = 2, 16, 32, 2, 128
+    a.dtype, a.scale = _td.TD_BF16, 0.0
+    a.q = a.k_blk = a.v_blk = a.k_ctx = a.v_ctx = a.ctx_offsets = a.out = FAKE
+    a.total_ctx, a.max_ctx = 3000, 2000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def commit(**kw):
+    c = _td.TdCommitArgs()
+    c.B, c.S, c.V, c.dtype, c.gamma = 2, 16, 131072, _td.TD_BF16, 0.8
+    c.logits = c.commit = c.token = FAKE
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(S=65), INVALID),
+    (dict(Hq=30, Hkv=4), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(dtype=7), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(total_ctx=-1), INVALID), (dict(max_ctx=4000), INVALID),
+    (dict(total_ctx=5000, max_ctx=2000), INVALID),
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(ctx_offsets=None), INVALID),
+    (dict(k_ctx=None), INVALID), (dict(B=70000), UNSUPPORTED), (dict(Hq=256, Hkv=2), UNSUPPORTED),
+])
+def test_attn_validation(L, kw, rc):
+    a = attn(**kw)
+    assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == rc
+
+
+def test_attn_empty_context_needs_no_context_pointers(L):
+    a = attn(k_ctx=None, v_ctx=None, total_ctx=0, max_ctx=0)
+    assert L.td_attn_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_attn_workspace_checks(L):
+    a = attn()
+    need = L.td_attn_workspace_bytes(ctypes.byref(a))
+    assert need > 0 and need % 256 == 0
+    assert L.td_block_attn(ctypes.byref(a), None, need, None) == WORKSPACE
+    assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+    assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE + 16), need, None) == WORKSPACE
+    assert L.td_attn_workspace_bytes(None) == 0
+    assert L.td_attn_workspace_bytes(ctypes.byref(attn(B=0))) == 0
+
+
+def test_attn_workspace_covers_every_key():
+    """The split plan covers every key of the longest sequence once: the
+    workspace holds nchunks partial slots per (b, kv head, row group), and
+    nchunks * chunk >= max_ctx + S for the chunk the plan picks."""
+    L = td.lib()
+    for B, Lmax, S, Hq in [(64, 8192, 16, 32), (4, 65536, 16, 32), (8, 4096, 16, 32),
+                           (32, 2048, 64, 32), (3, 1000, 1, 32)]:
+        a = attn(B=B, S=S, Hq=Hq, total_ctx=B * Lmax, max_ctx=Lmax)
+        ws = L.td_attn_workspace_bytes(ctypes.byref(a))
+        rg = -(-(Hq // 2) * S // 256)
+        per_slot = 256 * 128 * 4 + 256 * 8
+        if ws:
+            nch = ws // (B * 2 * rg) // per_slot
+            assert nch >= 2
+            assert B * 2 * rg * nch * per_slot <= ws < B * 2 * rg * (nch + 1) * per_slot
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(S=65), INVALID), (dict(V=0), INVALID),
+    (dict(dtype=3), INVALID), (dict(gamma=float("inf")), INVALID),
+    (dict(gamma=float("nan")), INVALID), (dict(logits=None), INVALID),
+    (dict(commit=None), INVALID), (dict(token=None), INVALID),
+])
+def test_commit_validation(L, kw, rc):
+    c = commit(**kw)
+    assert L.td_commit(ctypes.byref(c), ctypes.c_void_p(FAKE), 1 << 40, None) == rc
+
+
+def test_commit_workspace_checks(L):
+    c = commit()
+    need = L.td_commit_workspace_bytes(ctypes.byref(c))
+    assert need >= 2 * 16 * 16 and need % 256 == 0
+    assert L.td_commit(ctypes.byref(c), None, need, None) == WORKSPACE
+    assert L.td_commit(ctypes.byref(c), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+
+
+def test_denoise_step_checks(L):
+    a, c = attn(), commit()
+    need = L.td_denoise_workspace_bytes(ctypes.byref(a), ctypes.byref(c))
+    assert need >= L.td_attn_workspace_bytes(ctypes.byref(a)) + L.td_commit_workspace_bytes(ctypes.byref(c))
+    c2 = commit(S=8)
+    assert L.td_denoise_step(ctypes.byref(a), ctypes.byref(c2), ctypes.c_void_p(FAKE), need, None) == INVALID
+    assert L.td_denoise_step(ctypes.byref(a), ctypes.byref(c), None, need, None) == WORKSPACE
+    a_bad = attn(D=96)
+    assert L.td_denoise_step(ctypes.byref(a_bad), ctypes.byref(c), ctypes.c_void_p(FAKE), need, None) == UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 16, 4, 64)
+    with pytest.raises(ValueError):
+        _td.attn_args(x, x, x, x, x, torch.zeros(2, dtype=torch.int64), x, 0, 0)

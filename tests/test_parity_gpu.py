@@ -1,0 +1,285 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes span several key tiles, several context chunks and ragged tails; the
+full-size workloads are checked on sampled sequences the oracle computes one
+by one.  Gates: see tests/gpu_util.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_lm_td_amd as td
+import oracle
+import synth
+from gpu_util import (check_attn, compare_commit, dev, f64, log, oracle_attn, oracle_commit,
+                      run_attn, run_commit, upload_attn, upload_commit)
+
+pytestmark = pytest.mark.gpu
+W = synth.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _no_chunk_override(monkeypatch):
+    monkeypatch.delenv("TD_ATTN_CHUNK", raising=False)
+    monkeypatch.delenv("TD_COMMIT_SPLIT", raising=False)
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def test_attn_tiny_f32():
+    w = W["tiny_f32_b1_ctx64"]
+    a = synth.make_attention_inputs(w, 1001)
+    log("case attn tiny_f32", w)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), "tiny_f32", fp32=True)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "f32"), (64, "bf16")])
+def test_attn_valu_path_other_shapes(D, dtype):
+    w = W["tiny_f32_b1_ctx64"].with_(B=3, D=D, dtype=dtype, Hq=6, Hkv=3, S=5)
+    a = synth.make_attention_inputs(w, 7, lengths=[0, 45, 70])
+    log("case attn valu", D, dtype)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), f"valu D={D} {dtype}", fp32=(dtype == "f32"))
+
+
+@pytest.mark.parametrize("chunk", [None, "64", "96"])
+def test_attn_bf16_ragged_small(chunk, monkeypatch):
+    """Empty context, a context shorter than a tile, ragged tails, several chunks."""
+    if chunk:
+        monkeypatch.setenv("TD_ATTN_CHUNK", chunk)
+    w = W["bf16_b8_ctx4k"].with_(B=5)
+    a = synth.make_attention_inputs(w, 17, lengths=[0, 37, 1000, 513, 2])
+    log("case attn ragged small chunk", chunk)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), f"ragged small chunk={chunk}")
+
+
+@pytest.mark.parametrize("S,Hq,Hkv", [(1, 32, 2), (16, 32, 2), (32, 32, 2), (64, 32, 2),
+                                      (16, 8, 8), (16, 64, 1), (7, 12, 3), (3, 4, 1)])
+def test_attn_bf16_shapes(S, Hq, Hkv):
+    """Decode (S=1), S=32/64 (several row groups), MHA (G=1), G=64, odd sizes."""
+    w = W["bf16_b8_ctx4k"].with_(B=3, S=S, Hq=Hq, Hkv=Hkv)
+    a = synth.make_attention_inputs(w, 100 + S + Hq, lengths=[300, 0, 777])
+    log("case attn shape", S, Hq, Hkv)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), f"S={S} Hq={Hq} Hkv={Hkv}")
+
+
+def test_attn_unit_variance_and_scale():
+    w = W["bf16_b4_ctx64k"].with_(B=2)
+    a = synth.make_attention_inputs(w, 23, lengths=[1500, 2100])
+    d = upload_attn(a)
+    log("case attn unit variance + explicit scale")
+    check_attn(run_attn(d, a), oracle_attn(a), "unit variance")
+    check_attn(run_attn(d, a, scale=0.05), oracle_attn(a, scale=0.05), "scale=0.05")
+
+
+def test_attn_bf16_b8_ctx4k_full():
+    w = W["bf16_b8_ctx4k"]
+    a = synth.make_attention_inputs(w, 1002)
+    log("case attn bf16_b8_ctx4k full")
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), "bf16_b8_ctx4k (all sequences)")
+
+
+def test_attn_b64_ragged_sampled_and_deterministic():
+    w = W["bf16_b64_ragged1k_8k"]
+    a = synth.make_attention_inputs(w, 1003)
+    d = upload_attn(a)
+    log("case attn b64 ragged sampled, lengths", a["lengths"][:8])
+    got = run_attn(d, a)
+    seqs = [0, 17, int(np.argmax(a["lengths"])), int(np.argmin(a["lengths"])), 63]
+    check_attn(got[seqs], oracle_attn(a, seqs), f"b64 ragged sampled seqs={seqs}")
+    first = d["out"].clone()
+    run_attn(d, a)
+    assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
+
+
+def test_attn_b4_ctx64k_sampled():
+    w = W["bf16_b4_ctx64k"]
+    a = synth.make_attention_inputs(w, 1004)
+    log("case attn b4 ctx64k sampled")
+    got = run_attn(upload_attn(a), a)
+    check_attn(got[[2]], oracle_attn(a, [2]), "b4 ctx64k seq 2")
+
+
+@pytest.mark.parametrize("S", [16, 32, 64])
+def test_attn_loop_shapes_sampled(S):
+    w = W["bf16_b32_ctx2k_loop"].with_(S=S)
+    a = synth.make_attention_inputs(w, 1005 + S)
+    log("case attn loop shape S", S)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got[[0, 31]], oracle_attn(a, [0, 31]), f"b32 ctx2k S={S} seqs 0,31")
+
+
+# ----------------------------------------------------------------------------
+# commit
+# ----------------------------------------------------------------------------
+def _commit_case(w, seed, gamma, frac=1.0, seqs=None, label=""):
+    c = synth.make_commit_inputs(w, seed)
+    el = synth.make_eligible(w, seed, frac)
+    d = upload_commit(c["logits"], w.dtype, el)
+    g = run_commit(d, gamma)
+    ref = oracle_commit(c["logits"], w.dtype, el, gamma, seqs)
+    tok_in = np.full((w.B, w.S), -1)
+    return compare_commit(g, ref, el, gamma, tok_in, label or w.name, seqs)
+
+
+def test_commit_tiny_f32():
+    w = W["tiny_f32_b1_ctx64"]
+    log("case commit tiny f32")
+    _commit_case(w, 2001, w.gamma, label="tiny f32")
+
+
+@pytest.mark.parametrize("gamma", [0.5, 0.8, 0.95])
+def test_commit_b8_v131072(gamma):
+    w = W["bf16_b8_ctx4k"]
+    log("case commit b8 V131072 gamma", gamma)
+    _commit_case(w, 2002, gamma, frac=0.75, label=f"b8 gamma={gamma}")
+
+
+def test_commit_b64_sampled():
+    w = W["bf16_b64_ragged1k_8k"]
+    log("case commit b64 sampled")
+    _commit_case(w, 2003, 0.8, seqs=[0, 5, 31, 63], label="b64 sampled")
+
+
+def test_commit_b4_row_split():
+    """64 rows: each row is split over several workgroups."""
+    w = W["bf16_b4_ctx64k"]
+    log("case commit b4 (row split)")
+    _commit_case(w, 2004, 0.8, frac=0.9, label="b4 split rows")
+
+
+@pytest.mark.parametrize("V,dtype", [(1001, "bf16"), (1003, "f32"), (8, "bf16"), (1, "f32"),
+                                     (40000, "f32")])
+def test_commit_odd_vocab(V, dtype):
+    w = W["bf16_b8_ctx4k"].with_(B=3, S=9, V=V, dtype=dtype, logit_model="boost",
+                                 logit_std=1.0, margin_hi=6.0)
+    log("case commit odd vocab", V, dtype)
+    _commit_case(w, 2005 + V, 0.6, frac=0.8, label=f"V={V} {dtype}")
+
+
+def test_commit_ties_across_parts(monkeypatch):
+    """Equal maxima in different lanes / row parts: the lowest id wins."""
+    monkeypatch.setenv("TD_COMMIT_SPLIT", "4")
+    B, S, V = 2, 5, 131072
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((B, S, V)).astype(np.float32)
+    spots = [(0, 0, [5, 70000]), (0, 1, [131071, 65536, 40000]), (0, 2, [0, 1]),
+             (1, 3, [9, 17, 33000, 100000]), (1, 4, [32768, 32767])]
+    for b, i, ids in spots:
+        x[b, i, ids] = 9.0
+    bits = synth.f32_to_bf16_bits(x)
+    d = upload_commit(bits, "bf16", None)
+    g = run_commit(d, 0.5)
+    for b, i, ids in spots:
+        assert g["token"][b, i] == min(ids), (b, i, g["token"][b, i])
+    ref = oracle_commit(bits, "bf16", None, 0.5)
+    compare_commit(g, ref, None, 0.5, np.full((B, S), -1), "ties")
+
+
+@pytest.mark.parametrize("gamma", [1.5, 1e-6])
+def test_commit_extreme_gamma(gamma):
+    w = W["bf16_b8_ctx4k"].with_(V=4096)
+    log("case commit gamma", gamma)
+    c = synth.make_commit_inputs(w, 2010)
+    el = synth.make_eligible(w, 2010, 0.6)
+    el[3] = 0
+    d = upload_commit(c["logits"], "bf16", el)
+    g = run_commit(d, gamma)
+    n = g["commit"].sum(axis=1)
+    if gamma > 1:
+        assert (n == el.any(axis=1)).all()
+    else:
+        assert (g["commit"].astype(bool) == el.astype(bool)).all()
+    compare_commit(g, oracle_commit(c["logits"], "bf16", el, gamma), el, gamma,
+                   np.full((w.B, w.S), -1), f"gamma={gamma}")
+
+
+def test_commit_masked_inplace_and_tokens():
+    """masked_out aliasing masked_in; tokens keeps ids where nothing commits."""
+    w = W["bf16_b8_ctx4k"].with_(V=8192)
+    c = synth.make_commit_inputs(w, 2011)
+    el = synth.make_eligible(w, 2011, 0.7)
+    d = upload_commit(c["logits"], "bf16", el)
+    tok_in = np.arange(w.B * w.S, dtype=np.int32).reshape(w.B, w.S) + 1000000
+    d["tokens"].copy_(torch.from_numpy(tok_in))
+    d["masked_out"] = d["masked_in"]
+    g = run_commit(d, 0.8)
+    ref = oracle_commit(c["logits"], "bf16", el, 0.8)
+    compare_commit(g, ref, el, 0.8, tok_in, "in-place masks")
+
+
+# ----------------------------------------------------------------------------
+# denoise step and the block loop
+# ----------------------------------------------------------------------------
+def _step_inputs(w, seed, frac):
+    a = synth.make_attention_inputs(w, seed)
+    c = synth.make_commit_inputs(w, seed)
+    el = synth.make_eligible(w, seed, frac)
+    da = upload_attn(a)
+    dc = upload_commit(c["logits"], w.dtype, el)
+    return a, c, el, da, dc
+
+
+def _run_step(w, da, dc, a, gamma):
+    aa = td.attn_args(da["q"], da["k_blk"], da["v_blk"], da["k_ctx"], da["v_ctx"], da["offsets"],
+                      da["out"], a["total_ctx"], a["max_ctx"])
+    cc = td.commit_args(dc["logits"], dc["commit"], dc["token"], gamma, dc["masked_in"],
+                        dc["maxprob"], dc["n_commit"], dc["masked_out"], dc["tokens"],
+                        dc["n_masked_left"])
+    td.td_denoise_step(aa, cc, device=da["q"].device)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_b1_ctx64", "bf16_b8_ctx4k"])
+def test_denoise_step(name):
+    w = W[name]
+    a, c, el, da, dc = _step_inputs(w, 3001, 0.8)
+    log("case denoise step", name)
+    _run_step(w, da, dc, a, w.gamma)
+    got = da["out"].float().cpu().numpy().astype(np.float64)
+    ref = oracle.denoise_step({k: f64(a[k], w.dtype) if k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx")
+                               else a[k] for k in a}, f64(c["logits"], w.dtype), el,
+                              np.full((w.B, w.S), -1), w.gamma)
+    check_attn(got, ref["out"], f"step {name}", fp32=(w.dtype == "f32"))
+    g = {k: dc[k].cpu().numpy() for k in ("commit", "token", "maxprob", "n_commit", "masked_out",
+                                          "tokens", "n_masked_left")}
+    compare_commit(g, ref, el, w.gamma, np.full((w.B, w.S), -1), f"step {name}")
+
+
+@pytest.mark.parametrize("S,gamma", [(16, 0.5), (16, 0.8), (16, 0.95), (32, 0.5), (32, 0.8),
+                                     (32, 0.95), (64, 0.5), (64, 0.8), (64, 0.95)])
+def test_block_loop_teacher_forced(S, gamma):
+    """Whole-block loop: each step's commit is compared with the oracle's
+    commit from the same masked state; the loop ends within S steps."""
+    w = W["bf16_b32_ctx2k_loop"].with_(B=8, S=S, V=16384, gamma=gamma)
+    base, peak, stored = synth.loop_peak_values(w, 4000 + S, S + 1)
+    log("case loop S gamma", S, gamma)
+    logits = dev(base, "bf16").view(w.B, w.S, w.V)
+    rows = torch.arange(w.B * w.S, device="cuda")
+    peak_d = torch.from_numpy(peak).to("cuda")
+    masked = np.ones((w.B, w.S), np.uint8)
+    dc = upload_commit(base.reshape(w.B, w.S, w.V), "bf16", masked)
+    dc["logits"] = logits
+    tokens = np.full((w.B, w.S), -1)
+    steps = 0
+    while masked.any():
+        assert steps < S, "block did not finish within S steps"
+        logits.view(-1, w.V)[rows, peak_d] = dev(stored[steps], "bf16")
+        dc["masked_in"].copy_(torch.from_numpy(masked))
+        g = run_commit(dc, gamma)
+        x = synth.loop_step_logits(base, peak, stored, steps).reshape(w.B, w.S, w.V)
+        ref = oracle_commit(x, "bf16", masked, gamma)
+        compare_commit(g, ref, masked, gamma, tokens, f"loop S={S} g={gamma} step={steps}")
+        tokens = g["tokens"].astype(np.int64)
+        masked = g["masked_out"].copy()
+        assert int(g["n_masked_left"][0]) == int(masked.sum())
+        steps += 1
+    assert (tokens >= 0).all()
+    log(f"[loop] S={S} gamma={gamma}: steps={steps}")

@@ -5,20 +5,22 @@
 // bidirectional inside the block, layer-aligned cross-attention to the
 // per-layer KV cache; aiboss88.com, technical-principle section).
 //
-// bf16, D = 128: attn_bf16_mfma.  One workgroup owns up to 256 query rows
-// (the G heads x S positions that share one KV head, the GQA group) and one
-// chunk of the [context ; block] key sequence.  Four waves of 64 rows each.
-// K tiles are staged row-major in LDS, V tiles transposed (keys innermost),
-// and both products run on v_mfma_f32_32x32x16_bf16 in the transposed
-// orientation S^T = K Q^T, O^T = V^T P^T: the score matrix then lands with
-// one query per lane column, so the softmax max/sum over keys is 15 in-lane
-// ops plus one cross-half swap, and P^T feeds the PV product straight from
-// the accumulator registers (the key order inside a 16-key group is
-// permuted identically on both operands).  Softmax runs in the exp2 domain
-// with a lazy rescale: the running max only moves when a tile's max exceeds
-// it by more than 2^8, which is exact in real arithmetic and keeps P <= 256.
-// A chunk that is not the whole sequence writes fp32 partials (O, m, l);
-// attn_combine merges them by log-sum-exp in chunk order (deterministic).
+// bf16, D = 128: attn_bf16_mfma + attn_merge.  A workgroup of 8 waves owns
+// up to 256 query rows (the G heads x S positions that share one KV head,
+// the GQA group), 32 rows per wave, two waves per SIMD so that one wave's
+// softmax overlaps the other's matrix products.  K and V tiles of 64 keys
+// stream from HBM straight into a 4-stage LDS ring (16-byte global->LDS
+// DMA, two tiles in flight while one is consumed), stored row-major with
+// XOR-swizzled 16-byte chunks so every LDS read is bank-conflict free.  Both
+// products run on v_mfma_f32_32x32x16_bf16 in the transposed orientation
+// S^T = K Q^T, O^T = V^T P^T: the scores land with one query per lane, so the
+// softmax max/sum over keys is in-lane plus one cross-half swap, and P^T
+// feeds the PV product straight from the accumulator registers; the V^T
+// operand comes from row-major V through gfx950's transposing 8-byte LDS
+// reads.  The key order inside each 16-key step is permuted identically on
+// both operands.  Softmax runs in the exp2 domain with a lazy rescale: the
+// running max only moves when a tile's max exceeds it by more than 2^8,
+// which is exact in real arithmetic and keeps P <= 256.
 //
 // Any other dtype / head dim: attn_valu, one thread per query row (a plain
 // correctness path for small fp32 problems).
@@ -35,12 +37,20 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int HD = 128;                 // head dim of the MFMA path
-constexpr int KSTR = HD + 8;            // LDS row stride of the K tile (elements)
-constexpr int VSTR = kKeyTile + 8;      // LDS row stride of the V^T tile (elements)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazy = 8.0f;           // rescale only when the max grows by > 2^8
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier ordering LDS only.  Tiles arrive by global->LDS DMA whose
+// completion each wave checks with an explicit vmcnt wait before this
+// barrier; a full __syncthreads() would also drain the DMA still in flight
+// for the next tiles.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Clamped sequence range: never reads outside [0, total_ctx) whatever the
 // device offsets hold; L is also capped at max_ctx (the grid's assumption).
@@ -54,263 +64,402 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
   L = int(len > max_ctx ? max_ctx : len);
 }
 
-__global__ __launch_bounds__(256, 1) void attn_bf16_mfma(
+// ---------------------------------------------------------------------------
+// bf16 MFMA path: persistent, stream-K over 64-key tiles
+// ---------------------------------------------------------------------------
+// Work units are (sequence b, KV head g, row group rg); unit u owns the
+// ceil((L_b + S) / 64) key tiles of its sequence, and all units' tiles form
+// one global sequence of W tiles.  Each of the Pe = min(P, W) persistent
+// workgroups scans the ragged lengths itself (in LDS, no separate planning
+// launch) and walks an equal contiguous range of that sequence.  Units a
+// workgroup covers whole are normalised and written directly; where a range
+// cuts a unit, the workgroup writes a fp32 partial (O, m, l) into one of its
+// two slots, and attn_merge combines the partials of every cut unit after
+// the kernel (in workgroup order, so the result is deterministic).  Merging
+// in a second launch keeps the main kernel free of device-scope fences,
+// which on this part write back and invalidate a whole XCD's L2.
+constexpr int T = kKeyTile;       // keys per tile
+constexpr int NST = 4;            // LDS stages: tile t computes while t+1, t+2 land
+constexpr int TE = T * HD;        // elements of one K (or V) tile: 16 KB
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// 16-byte global->LDS DMA of one wave: lane i's 16 bytes from `src` land at
+// LDS byte address lds_base + 16*i.  Issued through asm so that the compiler
+// does not order later LDS reads behind it (completion is checked with
+// explicit vmcnt waits before the barrier that publishes a tile).  The asm
+// has no outputs.
+__device__ inline void dma16(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 1"
+               :
+               : "s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr(const void *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+__device__ inline int64_t wg_begin(int64_t p, int64_t W, int P) { return p * W / P; }
+// logical workgroup whose range holds global tile t
+__device__ inline int64_t tile_owner(int64_t t, int64_t W, int P) { return ((t + 1) * P - 1) / W; }
+// partial slot of workgroup pq holding its piece of a unit that starts at tile s_u
+__device__ inline int64_t piece_slot(int64_t pq, int64_t p_first, int64_t s_u, int64_t W, int P) {
+  return 2 * pq + ((pq == p_first && s_u != wg_begin(pq, W, P)) ? 1 : 0);
+}
+
+struct Cur {
+  int b, uis, j, n, L;
+  int64_t lo;
+};
+
+__device__ inline void cur_load(Cur &c, const int64_t *off, int64_t total, int max_ctx, int S) {
+  seq_range(off, c.b, total, max_ctx, c.lo, c.L);
+  c.n = (c.L + S + T - 1) / T;
+}
+__device__ inline void cur_next(Cur &c, int UPS, int B, const int64_t *off, int64_t total,
+                                int max_ctx, int S) {
+  if (++c.j < c.n) return;
+  c.j = 0;
+  if (++c.uis < UPS) return;
+  c.uis = 0;
+  if (++c.b < B) cur_load(c, off, total, max_ctx, S);
+}
+
+__global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const bf16 *__restrict__ q, const bf16 *__restrict__ kb, const bf16 *__restrict__ vb,
     const bf16 *__restrict__ kc, const bf16 *__restrict__ vc, const int64_t *__restrict__ off,
-    int64_t total_ctx, int max_ctx, int S, int Hq, int Hkv, int G, int M, int row_groups,
-    int chunk, int nchunks, float sl2, float *__restrict__ ws_o, float2 *__restrict__ ws_ml,
-    bf16 *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kKeyTile * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[HD * VSTR];
+    int64_t total_ctx, int max_ctx, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
+    float sl2, int64_t *__restrict__ prefix_out, float2 *__restrict__ ws_ml,
+    float *__restrict__ ws_o, bf16 *__restrict__ out) {
+  // K and V tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row:
+  // K chunk c of key r sits at c ^ (r % 16), V chunk c at c ^ 4*(r % 4).
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NST * TE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[NST * TE];
+  __shared__ int64_t s_scan[kWGThreads];
+  __shared__ int s_loc[3];
 
-  const int c = blockIdx.x;
-  const int g = blockIdx.y % Hkv;
-  const int rg = blockIdx.y / Hkv;
-  const int b = blockIdx.z;
-  int64_t lo;
-  int L;
-  seq_range(off, b, total_ctx, max_ctx, lo, L);
-  const int N = L + S;
-  const int k0 = c * chunk;
-  if (k0 >= N) return;
-  const int k1 = min(k0 + chunk, N);
-  const int nc_b = (N + chunk - 1) / chunk;
-
+  const int UPS = Hkv * RG;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
-  const int64_t kvstride = int64_t(Hkv) * HD;
+  // consecutive logical ranges land on one XCD (dispatch is round-robin over 8)
+  const int pid = (P % 8 == 0) ? int(blockIdx.x % 8) * (P / 8) + int(blockIdx.x / 8) : int(blockIdx.x);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane (query lq, half lh)
-  // holds Q[row][ks*16 + lh*8 .. +8] for the 8 k-steps of D = 128.
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = rg * kRowsPerWG + w * 64 + qb * 32 + lq;
-    if (row < M) {
-      const int s = row / G, j = row - s * G;
-      const bf16 *p = q + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + j) * HD + lh * 8;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(p + ks * 16);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = bf16x8{};
+  // ---- ragged plan: tiles per sequence, their prefix, this workgroup's start
+  auto ntiles = [&](int b) -> int64_t {
+    int64_t lo;
+    int L;
+    seq_range(off, b, total_ctx, max_ctx, lo, L);
+    return (int64_t(L) + S + T - 1) / T;
+  };
+  auto block_scan = [&]() {            // inclusive scan of s_scan in place
+    for (int d = 1; d < kWGThreads; d <<= 1) {
+      const int64_t v = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+  };
+  const bool one_pass = B <= kWGThreads;
+  int64_t n_mine = 0, wseq = 0;
+  if (one_pass) {
+    n_mine = tid < B ? ntiles(tid) : 0;
+    s_scan[tid] = n_mine;
+    __syncthreads();
+    block_scan();
+    wseq = s_scan[kWGThreads - 1];
+  } else {
+    for (int base = 0; base < B; base += kWGThreads) {
+      s_scan[tid] = base + tid < B ? ntiles(base + tid) : 0;
+      __syncthreads();
+      block_scan();
+      wseq += s_scan[kWGThreads - 1];
+      __syncthreads();
     }
   }
-
-  f32x16 o[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
-  float m[2] = {kNegInf, kNegInf};
-  float l[2] = {0.f, 0.f};
-
-  // ---- tile loaders (global -> registers), keys n in [k0, k1)
-  const bf16 *kc_g = kc + lo * kvstride + int64_t(g) * HD;
-  const bf16 *vc_g = vc + lo * kvstride + int64_t(g) * HD;
-  const bf16 *kb_g = kb + int64_t(b) * S * kvstride + int64_t(g) * HD;
-  const bf16 *vb_g = vb + int64_t(b) * S * kvstride + int64_t(g) * HD;
-  const int kr = tid >> 4, kc8 = (tid & 15) * 8;         // K: 2 x 16 B per thread
-  const int vk4 = tid >> 5, vd4 = (tid & 31) * 4;        // V: 4 keys x 4 dims per thread
-  uint4 kreg[2];
-  uint2 vreg[4];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int n = t + kr + r * 16;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (n < k1) {
-        const bf16 *src = n < L ? kc_g + int64_t(n) * kvstride : kb_g + int64_t(n - L) * kvstride;
-        x = *reinterpret_cast<const uint4 *>(src + kc8);
-      }
-      kreg[r] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = t + vk4 * 4 + i;
-      uint2 x = make_uint2(0, 0);
-      if (n < k1) {
-        const bf16 *src = n < L ? vc_g + int64_t(n) * kvstride : vb_g + int64_t(n - L) * kvstride;
-        x = *reinterpret_cast<const uint2 *>(src + vd4);
-      }
-      vreg[i] = x;
-    }
-  };
-  // V^T tile position of key k (0..31): within each 16-key group, key
-  // j*8 + h*4 + i (the accumulator's row order) goes to h*8 + j*4 + i, so a
-  // lane's 8 PV operand keys are contiguous.
-  const int vpos = (vk4 >> 2) * 16 + (vk4 & 1) * 8 + ((vk4 >> 1) & 1) * 4;
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      *reinterpret_cast<uint4 *>(&Ks[(kr + r * 16) * KSTR + kc8]) = kreg[r];
-    const uint32_t a0 = vreg[0].x, a1 = vreg[1].x, a2 = vreg[2].x, a3 = vreg[3].x;
-    const uint32_t b0 = vreg[0].y, b1 = vreg[1].y, b2 = vreg[2].y, b3 = vreg[3].y;
-    uint2 t0, t1, t2, t3;
-    t0.x = (a0 & 0xffffu) | (a1 << 16);          t0.y = (a2 & 0xffffu) | (a3 << 16);
-    t1.x = (a0 >> 16) | (a1 & 0xffff0000u);      t1.y = (a2 >> 16) | (a3 & 0xffff0000u);
-    t2.x = (b0 & 0xffffu) | (b1 << 16);          t2.y = (b2 & 0xffffu) | (b3 << 16);
-    t3.x = (b0 >> 16) | (b1 & 0xffff0000u);      t3.y = (b2 >> 16) | (b3 & 0xffff0000u);
-    *reinterpret_cast<uint2 *>(&Vt[(vd4 + 0) * VSTR + vpos]) = t0;
-    *reinterpret_cast<uint2 *>(&Vt[(vd4 + 1) * VSTR + vpos]) = t1;
-    *reinterpret_cast<uint2 *>(&Vt[(vd4 + 2) * VSTR + vpos]) = t2;
-    *reinterpret_cast<uint2 *>(&Vt[(vd4 + 3) * VSTR + vpos]) = t3;
-  };
-
-  load_tile(k0);
-  for (int t = k0; t < k1; t += kKeyTile) {
-    __syncthreads();                      // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (t + kKeyTile < k1) load_tile(t + kKeyTile);   // in flight during compute
-    const int nvalid = k1 - t;
-
-    // ---- S^T = K Q^T : 32 keys x 64 queries per wave (two 32x32 blocks)
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Ks[lq * KSTR + ks * 16 + lh * 8]);
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][ks], sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][ks], sc[1], 0, 0, 0);
-    }
-    if (nvalid < kKeyTile) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
-        if (key >= nvalid) { sc[0][r] = kNegInf; sc[1][r] = kNegInf; }
+  const int64_t W = wseq * UPS;
+  const int Pe = int(W < P ? W : P);          // logical workgroups with work
+  if (pid >= Pe) return;
+  const int64_t t_begin = wg_begin(pid, W, Pe), t_end = wg_begin(pid + 1, W, Pe);
+  if (pid == 0 && tid == 0) prefix_out[0] = 0;
+  if (one_pass) {
+    const int64_t incl = s_scan[tid], excl = incl - n_mine;
+    if (tid < B) {
+      if (pid == 0) prefix_out[tid + 1] = incl;
+      if (excl * UPS <= t_begin && t_begin < incl * UPS) {
+        const int64_t r = t_begin - excl * UPS;
+        s_loc[0] = tid; s_loc[1] = int(r / n_mine); s_loc[2] = int(r - (r / n_mine) * n_mine);
       }
     }
-
-    // ---- online softmax (exp2 domain, lazy rescale) and P^T as bf16
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = sc[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = mx * sl2;
-      const bool need = mxs > m[qb] + kLazy;
-      if (__any(need)) {
-        const float mn = need ? mxs : m[qb];
-        const float alpha = fast_exp2(m[qb] - mn);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-        l[qb] *= alpha;
-        m[qb] = mn;
-      }
-      float ls = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sc[qb][kk * 8 + i], sl2, -m[qb]));
-          ls += p;
-          pb[qb][kk][i] = bf16(p);
+  } else {
+    int64_t running = 0;
+    for (int base = 0; base < B; base += kWGThreads) {
+      const int b = base + tid;
+      const int64_t n = b < B ? ntiles(b) : 0;
+      s_scan[tid] = n;
+      __syncthreads();
+      block_scan();
+      const int64_t incl = running + s_scan[tid], excl = incl - n;
+      if (b < B) {
+        if (pid == 0) prefix_out[b + 1] = incl;
+        if (excl * UPS <= t_begin && t_begin < incl * UPS) {
+          const int64_t r = t_begin - excl * UPS;
+          s_loc[0] = b; s_loc[1] = int(r / n); s_loc[2] = int(r - (r / n) * n);
         }
       }
-      l[qb] += ls;
+      running += s_scan[kWGThreads - 1];
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int64_t kvs = int64_t(Hkv) * HD;
+
+  // ---- DMA issue of one tile: K and V rows w*8 .. w*8+7, two 4-row (1 KB) pieces each
+  auto issue = [&](const Cur &c, int stage) {
+    const int g = c.uis / RG;
+    const int k0 = c.j * T;
+    const int nvalid = min(T, c.L + S - k0);
+    const bf16 *kcg = kc + c.lo * kvs + int64_t(g) * HD;
+    const bf16 *vcg = vc + c.lo * kvs + int64_t(g) * HD;
+    const bf16 *kbg = kb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
+    const bf16 *vbg = vb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int R = w * 8 + r * 4 + (lane >> 4);        // tile row (key)
+      const int cs = lane & 15;                          // LDS chunk slot
+      const int key = k0 + (R < nvalid ? R : 0);         // rows past the end re-read a valid key
+      const int64_t roff = int64_t(key < c.L ? key : key - c.L) * kvs;
+      const bf16 *krow = (key < c.L ? kcg : kbg) + roff;
+      const bf16 *vrow = (key < c.L ? vcg : vbg) + roff;
+      const int ck = cs ^ (R & 15);
+      const int cv = cs ^ ((R & 3) << 2);
+      const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_addr(Ks + stage * TE + (w * 8 + r * 4) * HD));
+      const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_addr(Vs + stage * TE + (w * 8 + r * 4) * HD));
+      dma16(krow + ck * 8, kl);
+      dma16(vrow + cv * 8, vl);
+    }
+  };
+
+  Cur ld, cc;
+  ld.b = s_loc[0]; ld.uis = s_loc[1]; ld.j = s_loc[2];
+  cur_load(ld, off, total_ctx, max_ctx, S);
+  cc = ld;
+  issue(ld, 0);
+  cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
+  if (t_begin + 1 < t_end) {
+    issue(ld, 1);
+    cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
+  }
+
+  // per-lane LDS offsets (elements) of the MFMA operands
+  // K (A operand of S^T = K Q^T): key kb*32 + lq, chunk ks*2 + lh
+  // V (A operand of O^T = V^T P^T, via transposing reads): see below
+  const int e4 = (lane & 15) >> 2, a4 = lane & 3, gh = (lane >> 4) & 1;
+  const int v_lane_off = (lh * 4 + e4) * HD + gh * 16 + a4 * 4;
+
+  bf16x8 qf[8];
+  f32x16 o[4];
+  float m = kNegInf, l = 0.f;
+  int64_t seg_t0 = t_begin;
+  int seg_j0 = cc.j;
+
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int st = int((t - t_begin) & (NST - 1));
+    const int g = cc.uis / RG, rg = cc.uis - (cc.uis / RG) * RG;
+    const bool seg_begin = (t == t_begin) || cc.j == 0;
+    if (seg_begin) {
+      seg_t0 = t;
+      seg_j0 = cc.j;
+      const int row = rg * kRowsPerWG + w * 32 + lq;
+      if (row < M) {
+        const int s = row / G, jh = row - (row / G) * G;
+        const bf16 *p = q + ((int64_t(cc.b) * S + s) * Hq + int64_t(g) * G + jh) * HD + lh * 8;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(p + ks * 16);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8{};
+      }
+      // Q must have landed before the loop body's vmcnt bookkeeping (which
+      // counts only tile DMA) takes over; this drains tile t+1 once per segment.
+      __builtin_amdgcn_s_waitcnt(0xF70);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+      m = kNegInf;
+      l = 0.f;
+    }
+    if (t + 2 < t_end) {
+      issue(ld, (st + 2) & (NST - 1));
+      cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
+      __builtin_amdgcn_s_waitcnt(0xF70 | 8);    // tiles t+1, t+2 may stay in flight
+    } else if (t + 1 < t_end) {
+      __builtin_amdgcn_s_waitcnt(0xF70 | 4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xF70);
+    }
+    lds_barrier();
+
+    const int nvalid = min(T, cc.L + S - cc.j * T);
+    const bf16 *Kt = Ks + st * TE;
+    const bf16 *Vt = Vs + st * TE;
+
+    // ---- S^T = K Q^T : 64 keys x 32 queries (two 32x32 blocks)
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int row = kb2 * 32 + lq;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + row * HD + (((ks * 2 + lh) ^ (row & 15)) * 8));
+        sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sc[kb2], 0, 0, 0);
+      }
+    }
+    if (nvalid < T) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+          if (key >= nvalid) sc[kb2][r] = kNegInf;
+        }
     }
 
-    // ---- O^T += V^T P^T : 128 dims x 64 queries per wave
+    // ---- online softmax (exp2 domain, lazy rescale), P^T as bf16
+    float mx = sc[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * sl2;
+    const bool need = mxs > m + kLazy;
+    if (__any(need)) {
+      const float mn = need ? mxs : m;
+      const float alpha = fast_exp2(m - mn);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = mn;
+    }
+    bf16x8 pb[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + i], sl2, -m));
+        ls += p;
+        pb[kk][i] = bf16(p);
+      }
+    l += ls;
+
+    // ---- O^T += V^T P^T : V^T operand via two transposing 8-byte LDS reads
+    // (16-lane group g: source lane 4e+a addresses key (kk*16 + rd*8 +
+    // (g/2)*4 + e), dims db*32 + (g%2)*16 + 4a..+3; lane t of the group then
+    // holds dim db*32 + (g%2)*16 + t of those 4 keys)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8 *>(&Vt[(db * 32 + lq) * VSTR + kk * 16 + lh * 8]);
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[0][kk], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[1][kk], o[1][db], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int sw = (db ^ e4) * 32;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(Vt + (kk * 16 + 0) * HD + v_lane_off + sw));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(Vt + (kk * 16 + 8) * HD + v_lane_off + sw));
+        // whole-vector bit casts: building the operand element by element
+        // from the 16-bit lanes of the two reads does not compile correctly
+        const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+        const u32x4 a01 = {a0.x, a0.y, a1.x, a1.y};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, a01);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[db], 0, 0, 0);
       }
     }
-  }
 
+    // ---- end of a segment: whole unit -> output; cut unit -> partial (+ merge)
+    const bool seg_end = (t + 1 == t_end) || (cc.j == cc.n - 1);
+    if (seg_end) {
+      l += __shfl_xor(l, 32);
+      const int row = rg * kRowsPerWG + w * 32 + lq;
+      const int s = row / G, jh = row - (row / G) * G;
+      bf16 *dst = out + ((int64_t(cc.b) * S + s) * Hq + int64_t(g) * G + jh) * HD;
+      if (seg_j0 == 0 && cc.j == cc.n - 1) {
+        if (row < M) {
+          const float inv = 1.0f / l;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) l[qb] += __shfl_xor(l[qb], 32);
-
-  if (nc_b == 1) {
-    // The whole sequence is in this chunk: normalise and store bf16 (RNE).
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int row = rg * kRowsPerWG + w * 64 + qb * 32 + lq;
-      if (row >= M) continue;
-      const int s = row / G, j = row - s * G;
-      bf16 *dst = out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + j) * HD;
-      const float inv = 1.0f / l[qb];
+            for (int gi = 0; gi < 4; ++gi) {
+              bf16x4 v;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = bf16(o[qb][db][gi * 4 + e] * inv);
-          *reinterpret_cast<bf16x4 *>(dst + db * 32 + gi * 8 + lh * 4) = v;
+              for (int e = 0; e < 4; ++e) v[e] = bf16(o[db][gi * 4 + e] * inv);
+              *reinterpret_cast<bf16x4 *>(dst + db * 32 + gi * 8 + lh * 4) = v;
+            }
         }
+      } else {
+        const int64_t slot = 2 * int64_t(pid) + (seg_t0 == t_begin ? 0 : 1);
+        float4 *wo = reinterpret_cast<float4 *>(ws_o + slot * (kRowsPerWG * HD));
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi)
+            wo[((w * 4 + db) * 4 + gi) * 64 + lane] =
+                make_float4(o[db][gi * 4 + 0], o[db][gi * 4 + 1], o[db][gi * 4 + 2], o[db][gi * 4 + 3]);
+        if (lh == 0) ws_ml[slot * kRowsPerWG + w * 32 + lq] = make_float2(m, l);
+      }
     }
-  } else {
-    // Partials in accumulator-fragment order: float4 [frag][lane] per slot.
-    const size_t slot = (size_t(blockIdx.z * Hkv + g) * row_groups + rg) * nchunks + c;
-    float4 *wo = reinterpret_cast<float4 *>(ws_o + slot * (size_t(kRowsPerWG) * HD));
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int frag = ((w * 2 + qb) * 4 + db) * 4 + gi;
-          wo[frag * 64 + lane] = make_float4(o[qb][db][gi * 4 + 0], o[qb][db][gi * 4 + 1],
-                                             o[qb][db][gi * 4 + 2], o[qb][db][gi * 4 + 3]);
-        }
-    if (lh == 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        ws_ml[slot * kRowsPerWG + w * 64 + qb * 32 + lq] = make_float2(m[qb], l[qb]);
-    }
+    cur_next(cc, UPS, B, off, total_ctx, max_ctx, S);
   }
 }
 
-// Log-sum-exp merge of the chunk partials of every (b, kv head, row group)
-// whose sequence spans more than one chunk.  One thread per float4 of the
-// fragment layout; chunks merged in increasing order.
-__global__ __launch_bounds__(256) void attn_combine(
-    const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml, const int64_t *__restrict__ off,
-    int64_t total_ctx, int max_ctx, int S, int Hq, int Hkv, int G, int M, int row_groups,
-    int chunk, int nchunks, bf16 *__restrict__ out) {
-  const int unit = blockIdx.y;
-  const int rg = unit % row_groups;
-  const int g = (unit / row_groups) % Hkv;
-  const int b = unit / (row_groups * Hkv);
-  int64_t lo;
-  int L;
-  seq_range(off, b, total_ctx, max_ctx, lo, L);
-  const int N = L + S;
-  const int nc_b = (N + chunk - 1) / chunk;
-  if (nc_b <= 1) return;
-  const int f = blockIdx.x * 256 + threadIdx.x;      // 0 .. 8191
-  const int lane = f & 63, frag = f >> 6;
-  const int gi = frag & 3, db = (frag >> 2) & 3, qb = (frag >> 4) & 1, w = frag >> 5;
-  const int rloc = w * 64 + qb * 32 + (lane & 31);
-  const int row = rg * kRowsPerWG + rloc;
-  if (row >= M) return;
-  const size_t slot0 = size_t(unit) * nchunks;
-  float mmax = kNegInf;
-  for (int cc = 0; cc < nc_b; ++cc) mmax = fmaxf(mmax, ws_ml[(slot0 + cc) * kRowsPerWG + rloc].x);
-  float lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+
+// Merge of the partials of every unit cut between workgroups: one workgroup
+// per (unit, 32-row block); 4 float4 of the fragment layout per thread.
+__global__ __launch_bounds__(256) void attn_merge(
+    const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
+    const float2 *__restrict__ ws_ml, const float *__restrict__ ws_o, bf16 *__restrict__ out) {
+  const int UPS = Hkv * RG;
+  const int64_t u = blockIdx.x >> 3;
+  const int w = blockIdx.x & 7;
+  const int b = int(u / UPS), uis = int(u - (u / UPS) * UPS);
+  const int g = uis / RG, rg = uis - (uis / RG) * RG;
+  const int64_t W = prefix[B] * UPS;
+  const int Pe = int(W < P ? W : P);
+  const int64_t n = prefix[b + 1] - prefix[b];
+  const int64_t s_u = prefix[b] * UPS + int64_t(uis) * n, e_u = s_u + n;
+  const int64_t p_first = tile_owner(s_u, W, Pe), p_last = tile_owner(e_u - 1, W, Pe);
+  if (p_first == p_last) return;                 // written whole by its workgroup
   const float4 *wo = reinterpret_cast<const float4 *>(ws_o);
-  for (int cc = 0; cc < nc_b; ++cc) {
-    const float2 ml = ws_ml[(slot0 + cc) * kRowsPerWG + rloc];
-    const float wgt = fast_exp2(ml.x - mmax);
-    lsum += wgt * ml.y;
-    const float4 v = wo[(slot0 + cc) * (kRowsPerWG * HD / 4) + f];
-    acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int idx = int(threadIdx.x) + f * 256;
+    const int lane = idx & 63, frag = idx >> 6, db = frag >> 2, gi = frag & 3;
+    const int lq = lane & 31, lh = lane >> 5;
+    const int row = rg * kRowsPerWG + w * 32 + lq;
+    if (row >= M) continue;
+    float mm = kNegInf;
+    for (int64_t pq = p_first; pq <= p_last; ++pq) {
+      const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
+      mm = fmaxf(mm, ws_ml[sq * kRowsPerWG + w * 32 + lq].x);
+    }
+    float lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t pq = p_first; pq <= p_last; ++pq) {
+      const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
+      const float2 ml = ws_ml[sq * kRowsPerWG + w * 32 + lq];
+      const float wgt = fast_exp2(ml.x - mm);
+      lsum += wgt * ml.y;
+      const float4 v = wo[sq * (kRowsPerWG * HD / 4) + ((w * 4 + db) * 4 + gi) * 64 + lane];
+      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    }
+    const float inv = 1.0f / lsum;
+    const int s = row / G, jh = row - (row / G) * G;
+    bf16x4 o4;
+    o4[0] = bf16(acc.x * inv); o4[1] = bf16(acc.y * inv); o4[2] = bf16(acc.z * inv); o4[3] = bf16(acc.w * inv);
+    *reinterpret_cast<bf16x4 *>(out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + jh) * HD +
+                                db * 32 + gi * 8 + lh * 4) = o4;
   }
-  const float inv = 1.0f / lsum;
-  const int s = row / G, j = row - s * G;
-  const int d = db * 32 + gi * 8 + (lane >> 5) * 4;
-  bf16x4 v;
-  v[0] = bf16(acc.x * inv); v[1] = bf16(acc.y * inv); v[2] = bf16(acc.z * inv); v[3] = bf16(acc.w * inv);
-  *reinterpret_cast<bf16x4 *>(out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + j) * HD + d) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -397,21 +546,19 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int max_ctx = int(a->max_ctx);
   if (p.mfma) {
-    float *ws_o = reinterpret_cast<float *>(ws);
-    float2 *ws_ml = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + p.ws_o_bytes);
-    dim3 grid(p.nchunks, a->Hkv * p.row_groups, a->B);
-    hipLaunchKernelGGL(attn_bf16_mfma, grid, dim3(kWGThreads), 0, st,
+    char *wsb = static_cast<char *>(ws);
+    int64_t *prefix = reinterpret_cast<int64_t *>(wsb + p.off_prefix);
+    float2 *ws_ml = reinterpret_cast<float2 *>(wsb + p.off_ml);
+    float *ws_o = reinterpret_cast<float *>(wsb + p.off_o);
+    hipLaunchKernelGGL(attn_bf16_mfma, dim3(p.grid), dim3(kWGThreads), 0, st,
                        static_cast<const bf16 *>(a->q), static_cast<const bf16 *>(a->k_blk),
                        static_cast<const bf16 *>(a->v_blk), static_cast<const bf16 *>(a->k_ctx),
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
-                       a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.chunk, p.nchunks,
-                       p.scale_log2, ws_o, ws_ml, static_cast<bf16 *>(a->out));
-    if (p.nchunks > 1) {
-      dim3 g2(kRowsPerWG * HD / 4 / 256, unsigned(p.units));
-      hipLaunchKernelGGL(attn_combine, g2, dim3(256), 0, st, ws_o, ws_ml, a->ctx_offsets,
-                         a->total_ctx, max_ctx, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups,
-                         p.chunk, p.nchunks, static_cast<bf16 *>(a->out));
-    }
+                       a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.grid, p.scale_log2,
+                       prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out));
+    hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
+                       a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.grid, ws_ml, ws_o,
+                       static_cast<bf16 *>(a->out));
   } else {
     dim3 grid(p.row_groups, a->Hkv, a->B);
 #define TD_VALU(T, DD)                                                                         \

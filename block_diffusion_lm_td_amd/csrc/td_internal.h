@@ -11,21 +11,24 @@ namespace td {
 
 // Tiling constants of the bf16 MFMA attention kernel.
 constexpr int kRowsPerWG = 256;   // query rows (G*S rows of one KV head) per workgroup
-constexpr int kKeyTile = 32;      // keys per LDS tile
-constexpr int kWGThreads = 256;   // 4 waves of 64
+constexpr int kKeyTile = 64;      // keys per LDS tile
+constexpr int kWaves = 8;         // 8 waves x 32 rows; two waves share each SIMD
+constexpr int kWGThreads = 64 * kWaves;
+constexpr int kGridWGs = 256;     // persistent grid: one workgroup per CU of MI355X
 
 // Launch plan of one td_block_attn call, derived on the host from sizes only.
 struct AttnPlan {
   bool mfma;            // bf16, D == 128: MFMA kernel; otherwise the VALU kernel
   int G;                // Hq / Hkv
   int M;                // G * S query rows per (b, kv head)
-  int row_groups;       // ceil(M / kRowsPerWG)   (MFMA path)
-  int chunk;            // keys per split (multiple of kKeyTile)      (MFMA path)
-  int nchunks;          // ceil((max_ctx + S) / chunk)                (MFMA path)
+  int row_groups;       // ceil(M / kRowsPerWG) (MFMA) or ceil(M / 64) (VALU)
+  int grid;             // persistent workgroups (MFMA path)
   int64_t units;        // B * Hkv * row_groups
-  size_t ws_o_bytes;    // partial O, fp32, per (unit, chunk)
-  size_t ws_ml_bytes;   // partial (m, l) per (unit, chunk, row)
-  size_t ws_bytes;      // total, 256-byte aligned pieces
+  // workspace pieces (byte offsets), MFMA path
+  size_t off_prefix;    // int64 [B+1]: tile prefix over sequences (for the merge)
+  size_t off_ml;        // float2 [2*grid][256]: partial (m, l)
+  size_t off_o;         // float [2*grid][256*128]: partial O
+  size_t ws_bytes;      // total
   float scale_log2;     // scale * log2(e)
 };
 

@@ -15,6 +15,8 @@ int validate_attn(const td_attn_args *a, bool check_ptrs) {
   if (!a) return TD_ERR_INVALID;
   if (a->B < 1 || a->S < 1 || a->S > 64 || a->Hq < 1 || a->Hkv < 1) return TD_ERR_INVALID;
   if (a->B > 65535 || a->Hkv > 4096) return TD_ERR_UNSUPPORTED;   // launch-grid limits
+  if (int64_t(a->B) * a->Hkv * ((int64_t(a->Hq / a->Hkv) * a->S + 255) / 256) > (int64_t(1) << 30))
+    return TD_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv != 0) return TD_ERR_INVALID;
   if (a->Hq / a->Hkv > 64) return TD_ERR_UNSUPPORTED;
   if (a->dtype != TD_F32 && a->dtype != TD_BF16) return TD_ERR_INVALID;
@@ -46,25 +48,10 @@ int validate_commit(const td_commit_args *c, bool check_ptrs) {
   return TD_OK;
 }
 
-// Keys per split.  The grid should hold well over 256 workgroups (one per
-// CU at the kernel's register footprint) so that ragged sequences balance;
-// each split costs 128 KB of fp32 partials written and read back, so splits
-// are kept >= 512 keys (256 KB of K/V read) unless the problem is tiny.
-static int choose_chunk(const td_attn_args *a, int row_groups) {
-  const char *env = getenv("TD_ATTN_CHUNK");
-  if (env) {
-    int v = atoi(env);
-    if (v >= kKeyTile) return (v / kKeyTile) * kKeyTile;
-  }
-  int64_t keys = (a->total_ctx + int64_t(a->B) * a->S) * a->Hkv * row_groups;
-  int64_t target_wg = 1024;
-  int64_t ch = (keys + target_wg - 1) / target_wg;
-  ch = std::max<int64_t>(ch, 512);
-  ch = std::min<int64_t>(ch, 4096);
-  ch = (ch + kKeyTile - 1) / kKeyTile * kKeyTile;
-  int64_t nmax = a->max_ctx + a->S;
-  if (ch > nmax) ch = (nmax + kKeyTile - 1) / kKeyTile * kKeyTile;
-  return int(std::max<int64_t>(ch, kKeyTile));
+static int grid_wgs() {
+  const char *env = getenv("TD_ATTN_GRID");
+  if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);
+  return kGridWGs;
 }
 
 AttnPlan plan_attn(const td_attn_args *a) {
@@ -76,21 +63,18 @@ AttnPlan plan_attn(const td_attn_args *a) {
   p.scale_log2 = scale * 1.4426950408889634f;
   if (p.mfma) {
     p.row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
-    p.chunk = choose_chunk(a, p.row_groups);
-    p.nchunks = int((a->max_ctx + a->S + p.chunk - 1) / p.chunk);
+    p.grid = grid_wgs();
     p.units = int64_t(a->B) * a->Hkv * p.row_groups;
-    if (p.nchunks > 1) {
-      size_t per = size_t(kRowsPerWG) * 128 * sizeof(float);
-      p.ws_o_bytes = align256(size_t(p.units) * p.nchunks * per);
-      p.ws_ml_bytes = align256(size_t(p.units) * p.nchunks * kRowsPerWG * 2 * sizeof(float));
-    }
+    size_t o = 0;
+    p.off_prefix = o; o += align256(size_t(a->B + 1) * 8);
+    p.off_ml = o;     o += align256(size_t(2) * p.grid * kRowsPerWG * 8);
+    p.off_o = o;      o += align256(size_t(2) * p.grid * kRowsPerWG * 128 * 4);
+    p.ws_bytes = o;
   } else {
     p.row_groups = (p.M + 63) / 64;
-    p.chunk = 0;
-    p.nchunks = 1;
     p.units = int64_t(a->B) * a->Hkv * p.row_groups;
+    p.ws_bytes = 0;
   }
-  p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   return p;
 }
 

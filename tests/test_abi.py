@@ -68,36 +68,29 @@ def test_attn_validation(L, kw, rc):
 
 
 def test_attn_empty_context_needs_no_context_pointers(L):
+    """total_ctx = 0: null context pointers pass validation (only the
+    workspace check then stops the call, before any launch)."""
     a = attn(k_ctx=None, v_ctx=None, total_ctx=0, max_ctx=0)
-    assert L.td_attn_workspace_bytes(ctypes.byref(a)) == 0
-
-
-def test_attn_workspace_checks(L):
-    a = attn()
     need = L.td_attn_workspace_bytes(ctypes.byref(a))
-    assert need > 0 and need % 256 == 0
-    assert L.td_block_attn(ctypes.byref(a), None, need, None) == WORKSPACE
+    assert need > 0
     assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
-    assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE + 16), need, None) == WORKSPACE
-    assert L.td_attn_workspace_bytes(None) == 0
-    assert L.td_attn_workspace_bytes(ctypes.byref(attn(B=0))) == 0
 
 
-def test_attn_workspace_covers_every_key():
-    """The split plan covers every key of the longest sequence once: the
-    workspace holds nchunks partial slots per (b, kv head, row group), and
-    nchunks * chunk >= max_ctx + S for the chunk the plan picks."""
-    L = td.lib()
+def test_attn_workspace_bytes(L):
+    """bf16 / D=128 (MFMA path): a persistent grid of 256 workgroups, each
+    with two fp32 partial slots (256 x 128 O values + 256 (m, l) pairs),
+    plus per-sequence, per-workgroup and per-unit tables.  The size depends
+    on the batch shape only, never on the context lengths."""
+    slot = 256 * 128 * 4 + 256 * 8
     for B, Lmax, S, Hq in [(64, 8192, 16, 32), (4, 65536, 16, 32), (8, 4096, 16, 32),
                            (32, 2048, 64, 32), (3, 1000, 1, 32)]:
         a = attn(B=B, S=S, Hq=Hq, total_ctx=B * Lmax, max_ctx=Lmax)
         ws = L.td_attn_workspace_bytes(ctypes.byref(a))
-        rg = -(-(Hq // 2) * S // 256)
-        per_slot = 256 * 128 * 4 + 256 * 8
-        if ws:
-            nch = ws // (B * 2 * rg) // per_slot
-            assert nch >= 2
-            assert B * 2 * rg * nch * per_slot <= ws < B * 2 * rg * (nch + 1) * per_slot
+        assert 2 * 256 * slot <= ws <= 2 * 256 * slot + 64 * 1024 + B * 64
+        a2 = attn(B=B, S=S, Hq=Hq, total_ctx=B * 7, max_ctx=7)
+        assert L.td_attn_workspace_bytes(ctypes.byref(a2)) == ws
+    f = attn(dtype=_td.TD_F32, D=64)
+    assert L.td_attn_workspace_bytes(ctypes.byref(f)) == 0   # VALU path needs none
 
 
 @pytest.mark.parametrize("kw,rc", [

@@ -22,7 +22,7 @@ W = synth.WORKLOADS
 
 @pytest.fixture(autouse=True)
 def _no_chunk_override(monkeypatch):
-    monkeypatch.delenv("TD_ATTN_CHUNK", raising=False)
+    monkeypatch.delenv("TD_ATTN_GRID", raising=False)
     monkeypatch.delenv("TD_COMMIT_SPLIT", raising=False)
 
 
@@ -46,16 +46,18 @@ def test_attn_valu_path_other_shapes(D, dtype):
     check_attn(got, oracle_attn(a), f"valu D={D} {dtype}", fp32=(dtype == "f32"))
 
 
-@pytest.mark.parametrize("chunk", [None, "64", "96"])
-def test_attn_bf16_ragged_small(chunk, monkeypatch):
-    """Empty context, a context shorter than a tile, ragged tails, several chunks."""
-    if chunk:
-        monkeypatch.setenv("TD_ATTN_CHUNK", chunk)
+@pytest.mark.parametrize("grid", [None, "1", "3", "37", "1000"])
+def test_attn_bf16_ragged_small(grid, monkeypatch):
+    """Empty context, a context shorter than a tile, ragged tails; the
+    persistent grid size varies from one workgroup (no split unit) to more
+    workgroups than key tiles (every unit split many ways)."""
+    if grid:
+        monkeypatch.setenv("TD_ATTN_GRID", grid)
     w = W["bf16_b8_ctx4k"].with_(B=5)
     a = synth.make_attention_inputs(w, 17, lengths=[0, 37, 1000, 513, 2])
-    log("case attn ragged small chunk", chunk)
+    log("case attn ragged small grid", grid)
     got = run_attn(upload_attn(a), a)
-    check_attn(got, oracle_attn(a), f"ragged small chunk={chunk}")
+    check_attn(got, oracle_attn(a), f"ragged small grid={grid}")
 
 
 @pytest.mark.parametrize("S,Hq,Hkv", [(1, 32, 2), (16, 32, 2), (32, 32, 2), (64, 32, 2),

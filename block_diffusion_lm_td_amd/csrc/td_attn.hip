@@ -79,7 +79,7 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
 // in a second launch keeps the main kernel free of device-scope fences,
 // which on this part write back and invalidate a whole XCD's L2.
 constexpr int T = kKeyTile;       // keys per tile
-constexpr int NST = 4;            // LDS stages: tile t computes while t+1, t+2 land
+constexpr int NST = 4;            // LDS stages: tiles t-1 (its B half), t, and t+1, t+2 landing
 constexpr int TE = T * HD;        // elements of one K (or V) tile: 16 KB
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -125,6 +125,76 @@ __device__ inline void cur_next(Cur &c, int UPS, int B, const int64_t *off, int6
   if (++c.uis < UPS) return;
   c.uis = 0;
   if (++c.b < B) cur_load(c, off, total, max_ctx, S);
+}
+
+// ---- half-tile pieces (32 keys) of the per-tile pipeline
+// QK for keys h*32 .. h*32+31 of the tile: S^T half = K Q^T (one 32x32 block)
+__device__ __forceinline__ void qk_half(const bf16 *__restrict__ Kt, int h, int lq, int lh,
+                                        const bf16x8 (&qf)[8], f32x16 &s) {
+  s = f32x16{};
+  const int row = h * 32 + lq;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + row * HD + (((ks * 2 + lh) ^ (row & 15)) * 8));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+  }
+}
+// softmax of a half: P^T as bf16 (k-steps kk = 0, 1 of the half) and its lane sum
+__device__ __forceinline__ float sm_half(const f32x16 &s, float m, float sl2, bf16x8 (&p)[2]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pv = fast_exp2(__builtin_fmaf(s[kk * 8 + i], sl2, -m));
+      acc += pv;
+      p[kk][i] = bf16(pv);
+    }
+  return acc;
+}
+// O^T += V^T P^T for keys h*32 .. h*32+31; the V^T operand comes from two
+// transposing 8-byte LDS reads (16-lane group g: source lane 4e+a addresses
+// key (k-step*16 + rd*8 + (g/2)*4 + e), dims db*32 + (g%2)*16 + 4a..+3; lane t
+// of the group then holds dim db*32 + (g%2)*16 + t of those 4 keys)
+__device__ __forceinline__ void pv_half(const bf16 *__restrict__ Vt, int h, int e4, int v_lane_off,
+                                        const bf16x8 (&p)[2], f32x16 (&o)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int sw = (db ^ e4) * 32;
+      const bf16 *base = Vt + (h * 2 + kk) * 16 * HD + v_lane_off + sw;
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base));
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + 8 * HD));
+      // whole-vector bit casts: building the operand element by element
+      // from the 16-bit lanes of the two reads does not compile correctly
+      const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+      const u32x4 a01 = {a0.x, a0.y, a1.x, a1.y};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, a01);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[db], 0, 0, 0);
+    }
+}
+// P *= alpha in place (bf16), used when the running max moves while P waits
+__device__ __forceinline__ void scale_p(bf16x8 (&p)[2], float alpha) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[kk][i] = bf16(float(p[kk][i]) * alpha);
+}
+// row max of a half (both lane halves hold the same query), in the exp2 domain
+__device__ __forceinline__ float max_half(const f32x16 &s, float sl2) {
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  return fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+}
+// keys h*32 + key >= nvalid get a score of -inf
+__device__ __forceinline__ void mask_half(f32x16 &s, int h, int lh, int nvalid) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = h * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+    if (key >= nvalid) s[r] = kNegInf;
+  }
 }
 
 __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
@@ -225,20 +295,28 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const bf16 *vcg = vc + c.lo * kvs + int64_t(g) * HD;
     const bf16 *kbg = kb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
     const bf16 *vbg = vb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
+    const bool fast = k0 + T <= c.L;               // whole tile in the context cache
+    const int64_t fbase = (c.lo + k0) * kvs + int64_t(g) * HD;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int R = w * 8 + r * 4 + (lane >> 4);        // tile row (key)
       const int cs = lane & 15;                          // LDS chunk slot
-      const int key = k0 + (R < nvalid ? R : 0);         // rows past the end re-read a valid key
-      const int64_t roff = int64_t(key < c.L ? key : key - c.L) * kvs;
-      const bf16 *krow = (key < c.L ? kcg : kbg) + roff;
-      const bf16 *vrow = (key < c.L ? vcg : vbg) + roff;
       const int ck = cs ^ (R & 15);
       const int cv = cs ^ ((R & 3) << 2);
+      const bf16 *ksrc, *vsrc;
+      if (fast) {
+        ksrc = kc + fbase + int64_t(R) * kvs + ck * 8;
+        vsrc = vc + fbase + int64_t(R) * kvs + cv * 8;
+      } else {
+        const int key = k0 + (R < nvalid ? R : 0);       // rows past the end re-read a valid key
+        const int64_t roff = int64_t(key < c.L ? key : key - c.L) * kvs;
+        ksrc = (key < c.L ? kcg : kbg) + roff + ck * 8;
+        vsrc = (key < c.L ? vcg : vbg) + roff + cv * 8;
+      }
       const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_addr(Ks + stage * TE + (w * 8 + r * 4) * HD));
       const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_addr(Vs + stage * TE + (w * 8 + r * 4) * HD));
-      dma16(krow + ck * 8, kl);
-      dma16(vrow + cv * 8, vl);
+      dma16(ksrc, kl);
+      dma16(vsrc, vl);
     }
   };
 
@@ -246,10 +324,8 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   ld.b = s_loc[0]; ld.uis = s_loc[1]; ld.j = s_loc[2];
   cur_load(ld, off, total_ctx, max_ctx, S);
   cc = ld;
-  issue(ld, 0);
-  cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
-  if (t_begin + 1 < t_end) {
-    issue(ld, 1);
+  for (int x = 0; x < 2 && t_begin + x < t_end; ++x) {
+    issue(ld, x);
     cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
   }
 
@@ -261,17 +337,58 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
 
   bf16x8 qf[8];
   f32x16 o[4];
+  f32x16 sA, sB;                 // scores of the two 32-key halves of a tile
+  bf16x8 pA[2], pB[2];
   float m = kNegInf, l = 0.f;
-  int64_t seg_t0 = t_begin;
-  int seg_j0 = cc.j;
 
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const int st = int((t - t_begin) & (NST - 1));
+  // Moves the running max when the half's max exceeds it by more than 2^8
+  // (lazy rescale: exact in real arithmetic, keeps P <= 256).  O must hold
+  // exactly the products made with the old max when this runs.
+  auto lazy = [&](float mxs, float &alpha) -> bool {
+    const bool need = mxs > m + kLazy;
+    if (__any(need)) {
+      const float mn = need ? mxs : m;
+      alpha = fast_exp2(m - mn);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = mn;
+      return true;
+    }
+    return false;
+  };
+
+  // Per tile t (halves A = keys 0-31, B = keys 32-63), three phases whose
+  // matrix work and softmax work are independent:
+  //   1: QK_A(t)                 || softmax B(t-1)
+  //   2: QK_B(t) + PV_B(t-1)     || softmax A(t)
+  //   3: PV_A(t)
+  // A segment's first tile has no B(t-1); the B half of its last tile is
+  // finished right after that tile's phase 3.  Each phase is one basic block.
+  int64_t t = t_begin;
+  int st = 0;
+  // wait for tile t (only tile t+1 may still be in flight), publish it, and
+  // refill the stage of tile t-2 with tile t+2
+  auto next_tile = [&]() {
+    if (t + 1 < t_end) {
+      __builtin_amdgcn_s_waitcnt(0xF70 | 4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xF70);
+    }
+    lds_barrier();
+    if (t + 2 < t_end) {
+      issue(ld, (st + 2) & (NST - 1));
+      cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
+    }
+  };
+  while (t < t_end) {
+    // ---- segment: this WG's tiles of one unit
     const int g = cc.uis / RG, rg = cc.uis - (cc.uis / RG) * RG;
-    const bool seg_begin = (t == t_begin) || cc.j == 0;
-    if (seg_begin) {
-      seg_t0 = t;
-      seg_j0 = cc.j;
+    const int64_t seg_t0 = t;
+    const int seg_j0 = cc.j;
+    const int64_t seg_t1 = min(t_end, t + (cc.n - cc.j));     // one past the segment's last tile
+    const Cur cu = cc;                                         // the segment's unit
+    {
       const int row = rg * kRowsPerWG + w * 32 + lq;
       if (row < M) {
         const int s = row / G, jh = row - (row / G) * G;
@@ -282,137 +399,100 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8{};
       }
-      // Q must have landed before the loop body's vmcnt bookkeeping (which
-      // counts only tile DMA) takes over; this drains tile t+1 once per segment.
-      __builtin_amdgcn_s_waitcnt(0xF70);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-      m = kNegInf;
-      l = 0.f;
-    }
-    if (t + 2 < t_end) {
-      issue(ld, (st + 2) & (NST - 1));
-      cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
-      __builtin_amdgcn_s_waitcnt(0xF70 | 8);    // tiles t+1, t+2 may stay in flight
-    } else if (t + 1 < t_end) {
-      __builtin_amdgcn_s_waitcnt(0xF70 | 4);
-    } else {
+      // Q must have landed before the loop's vmcnt bookkeeping (which counts
+      // only tile DMA) takes over; this drains the tile in flight once per segment.
       __builtin_amdgcn_s_waitcnt(0xF70);
     }
-    lds_barrier();
-
-    const int nvalid = min(T, cc.L + S - cc.j * T);
-    const bf16 *Kt = Ks + st * TE;
-    const bf16 *Vt = Vs + st * TE;
-
-    // ---- S^T = K Q^T : 64 keys x 32 queries (two 32x32 blocks)
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int row = kb2 * 32 + lq;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + row * HD + (((ks * 2 + lh) ^ (row & 15)) * 8));
-        sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sc[kb2], 0, 0, 0);
-      }
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    m = kNegInf;
+    l = 0.f;
+
+    // first tile of the segment
+    float alpha;
+    next_tile();
+    int nvalid = min(T, cc.L + S - cc.j * T);
+    {
+      const bf16 *Kt = Ks + st * TE;
+      const bf16 *Vt = Vs + st * TE;
+      qk_half(Kt, 0, lq, lh, qf, sA);
+      if (nvalid < 32) mask_half(sA, 0, lh, nvalid);
+      lazy(max_half(sA, sl2), alpha);
+      qk_half(Kt, 1, lq, lh, qf, sB);
+      l += sm_half(sA, m, sl2, pA);
+      pv_half(Vt, 0, e4, v_lane_off, pA, o);
     }
-    if (nvalid < T) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb2 * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-          if (key >= nvalid) sc[kb2][r] = kNegInf;
-        }
+    // steady tiles: all full (only a segment's last tile can be partial)
+    auto steady = [&](bool may_mask) {
+      next_tile();
+      nvalid = min(T, cc.L + S - cc.j * T);
+      const bf16 *Kt = Ks + st * TE;
+      const bf16 *Vt = Vs + st * TE;
+      const bf16 *Vp = Vs + ((st + NST - 1) & (NST - 1)) * TE;
+      lazy(max_half(sB, sl2), alpha);
+      // phase 1
+      qk_half(Kt, 0, lq, lh, qf, sA);
+      l += sm_half(sB, m, sl2, pB);
+      if (may_mask && nvalid < 32) mask_half(sA, 0, lh, nvalid);
+      // the pending P_B was made with the old max
+      if (lazy(max_half(sA, sl2), alpha)) scale_p(pB, alpha);
+      // phases 2 and 3
+      qk_half(Kt, 1, lq, lh, qf, sB);
+      pv_half(Vp, 1, e4, v_lane_off, pB, o);
+      l += sm_half(sA, m, sl2, pA);
+      pv_half(Vt, 0, e4, v_lane_off, pA, o);
+    };
+    auto advance = [&]() {
+      ++t;
+      st = (st + 1) & (NST - 1);
+      cur_next(cc, UPS, B, off, total_ctx, max_ctx, S);
+    };
+    advance();
+    for (; t + 1 < seg_t1; advance()) steady(false);
+    if (t < seg_t1) {
+      steady(true);
+      advance();
     }
-
-    // ---- online softmax (exp2 domain, lazy rescale), P^T as bf16
-    float mx = sc[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * sl2;
-    const bool need = mxs > m + kLazy;
-    if (__any(need)) {
-      const float mn = need ? mxs : m;
-      const float alpha = fast_exp2(m - mn);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      l *= alpha;
-      m = mn;
+    // B half of the segment's last tile (stage st - 1), then the output
+    {
+      const int stl = (st + NST - 1) & (NST - 1);
+      const bf16 *Vl = Vs + stl * TE;
+      if (nvalid < T) mask_half(sB, 1, lh, nvalid);
+      lazy(max_half(sB, sl2), alpha);
+      l += sm_half(sB, m, sl2, pB);
+      pv_half(Vl, 1, e4, v_lane_off, pB, o);
     }
-    bf16x8 pb[4];
-    float ls = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sc[kk >> 1][(kk & 1) * 8 + i], sl2, -m));
-        ls += p;
-        pb[kk][i] = bf16(p);
-      }
-    l += ls;
-
-    // ---- O^T += V^T P^T : V^T operand via two transposing 8-byte LDS reads
-    // (16-lane group g: source lane 4e+a addresses key (kk*16 + rd*8 +
-    // (g/2)*4 + e), dims db*32 + (g%2)*16 + 4a..+3; lane t of the group then
-    // holds dim db*32 + (g%2)*16 + t of those 4 keys)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int sw = (db ^ e4) * 32;
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t *)(Vt + (kk * 16 + 0) * HD + v_lane_off + sw));
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t *)(Vt + (kk * 16 + 8) * HD + v_lane_off + sw));
-        // whole-vector bit casts: building the operand element by element
-        // from the 16-bit lanes of the two reads does not compile correctly
-        const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
-        const u32x4 a01 = {a0.x, a0.y, a1.x, a1.y};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, a01);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[db], 0, 0, 0);
-      }
-    }
-
-    // ---- end of a segment: whole unit -> output; cut unit -> partial (+ merge)
-    const bool seg_end = (t + 1 == t_end) || (cc.j == cc.n - 1);
-    if (seg_end) {
-      l += __shfl_xor(l, 32);
-      const int row = rg * kRowsPerWG + w * 32 + lq;
-      const int s = row / G, jh = row - (row / G) * G;
-      bf16 *dst = out + ((int64_t(cc.b) * S + s) * Hq + int64_t(g) * G + jh) * HD;
-      if (seg_j0 == 0 && cc.j == cc.n - 1) {
-        if (row < M) {
-          const float inv = 1.0f / l;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-              bf16x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = bf16(o[db][gi * 4 + e] * inv);
-              *reinterpret_cast<bf16x4 *>(dst + db * 32 + gi * 8 + lh * 4) = v;
-            }
-        }
-      } else {
-        const int64_t slot = 2 * int64_t(pid) + (seg_t0 == t_begin ? 0 : 1);
-        float4 *wo = reinterpret_cast<float4 *>(ws_o + slot * (kRowsPerWG * HD));
+    l += __shfl_xor(l, 32);
+    const int row = rg * kRowsPerWG + w * 32 + lq;
+    const int last_j = seg_j0 + int(seg_t1 - seg_t0) - 1;
+    if (seg_j0 == 0 && last_j == cu.n - 1) {               // the whole unit: output
+      if (row < M) {
+        const int s = row / G, jh = row - (row / G) * G;
+        bf16 *dst = out + ((int64_t(cu.b) * S + s) * Hq + int64_t(g) * G + jh) * HD;
+        const float inv = 1.0f / l;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int gi = 0; gi < 4; ++gi)
-            wo[((w * 4 + db) * 4 + gi) * 64 + lane] =
-                make_float4(o[db][gi * 4 + 0], o[db][gi * 4 + 1], o[db][gi * 4 + 2], o[db][gi * 4 + 3]);
-        if (lh == 0) ws_ml[slot * kRowsPerWG + w * 32 + lq] = make_float2(m, l);
+          for (int gi = 0; gi < 4; ++gi) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = bf16(o[db][gi * 4 + e] * inv);
+            *reinterpret_cast<bf16x4 *>(dst + db * 32 + gi * 8 + lh * 4) = v;
+          }
       }
+    } else {                                                   // a piece: partial slot
+      const int64_t slot = 2 * int64_t(pid) + (seg_t0 == t_begin ? 0 : 1);
+      float4 *wo = reinterpret_cast<float4 *>(ws_o + slot * (kRowsPerWG * HD));
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+          wo[((w * 4 + db) * 4 + gi) * 64 + lane] =
+              make_float4(o[db][gi * 4 + 0], o[db][gi * 4 + 1], o[db][gi * 4 + 2], o[db][gi * 4 + 3]);
+      if (lh == 0) ws_ml[slot * kRowsPerWG + w * 32 + lq] = make_float2(m, l);
     }
-    cur_next(cc, UPS, B, off, total_ctx, max_ctx, S);
   }
 }
-
 
 // Merge of the partials of every unit cut between workgroups: one workgroup
 // per (unit, 32-row block); 4 float4 of the fragment layout per thread.

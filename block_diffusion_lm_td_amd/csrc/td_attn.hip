@@ -73,7 +73,7 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
 // workgroups scans the ragged lengths itself (in LDS, no separate planning
 // launch) and walks an equal contiguous range of that sequence.  Units a
 // workgroup covers whole are normalised and written directly; where a range
-// cuts a unit, the workgroup writes a fp32 partial (O, m, l) into one of its
+// cuts a unit, the workgroup writes a partial (O / l in bf16, m, l) into one of its
 // two slots, and attn_merge combines the partials of every cut unit after
 // the kernel (in workgroup order, so the result is deterministic).  Merging
 // in a second launch keeps the main kernel free of device-scope fences,
@@ -99,6 +99,12 @@ __device__ inline void dma16(const void *src, uint32_t lds_base) {
 }
 __device__ inline uint32_t lds_addr(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// two floats -> two bf16 (round to nearest even), low half first
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  const bf16 x = bf16(a), y = bf16(b);
+  return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
 }
 
 __device__ inline int64_t wg_begin(int64_t p, int64_t W, int P) { return p * W / P; }
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const bf16 *__restrict__ kc, const bf16 *__restrict__ vc, const int64_t *__restrict__ off,
     int64_t total_ctx, int max_ctx, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     float sl2, int64_t *__restrict__ prefix_out, float2 *__restrict__ ws_ml,
-    float *__restrict__ ws_o, bf16 *__restrict__ out) {
+    bf16 *__restrict__ ws_o, bf16 *__restrict__ out) {
   // K and V tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row:
   // K chunk c of key r sits at c ^ (r % 16), V chunk c at c ^ 4*(r % 4).
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NST * TE];
@@ -481,24 +487,31 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
           }
       }
     } else {                                                   // a piece: partial slot
+      // O / l in bf16 (the merge weighs pieces by l * 2^(m - max m)); lane's
+      // 16 values of fragment db are 32 contiguous bytes
       const int64_t slot = 2 * int64_t(pid) + (seg_t0 == t_begin ? 0 : 1);
-      float4 *wo = reinterpret_cast<float4 *>(ws_o + slot * (kRowsPerWG * HD));
+      uint4 *wo = reinterpret_cast<uint4 *>(ws_o + slot * (kRowsPerWG * HD));
+      const float inv = 1.0f / l;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db) {
+        uint32_t h[8];
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          wo[((w * 4 + db) * 4 + gi) * 64 + lane] =
-              make_float4(o[db][gi * 4 + 0], o[db][gi * 4 + 1], o[db][gi * 4 + 2], o[db][gi * 4 + 3]);
+        for (int i = 0; i < 8; ++i) h[i] = pack_bf16(o[db][2 * i] * inv, o[db][2 * i + 1] * inv);
+        wo[((w * 4 + db) * 64 + lane) * 2 + 0] = make_uint4(h[0], h[1], h[2], h[3]);
+        wo[((w * 4 + db) * 64 + lane) * 2 + 1] = make_uint4(h[4], h[5], h[6], h[7]);
+      }
       if (lh == 0) ws_ml[slot * kRowsPerWG + w * 32 + lq] = make_float2(m, l);
     }
   }
 }
 
 // Merge of the partials of every unit cut between workgroups: one workgroup
-// per (unit, 32-row block); 4 float4 of the fragment layout per thread.
+// per (unit, 32-row block of one wave); thread (db, lane) combines the 16
+// values that lane held in fragment db, over the unit's pieces in workgroup
+// order with a running max (one pass, deterministic).
 __global__ __launch_bounds__(256) void attn_merge(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
-    const float2 *__restrict__ ws_ml, const float *__restrict__ ws_o, bf16 *__restrict__ out) {
+    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out) {
   const int UPS = Hkv * RG;
   const int64_t u = blockIdx.x >> 3;
   const int w = blockIdx.x & 7;
@@ -510,36 +523,44 @@ __global__ __launch_bounds__(256) void attn_merge(
   const int64_t s_u = prefix[b] * UPS + int64_t(uis) * n, e_u = s_u + n;
   const int64_t p_first = tile_owner(s_u, W, Pe), p_last = tile_owner(e_u - 1, W, Pe);
   if (p_first == p_last) return;                 // written whole by its workgroup
-  const float4 *wo = reinterpret_cast<const float4 *>(ws_o);
+  const int lane = threadIdx.x & 63, db = threadIdx.x >> 6;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int row = rg * kRowsPerWG + w * 32 + lq;
+  if (row >= M) return;
+  const uint4 *wo = reinterpret_cast<const uint4 *>(ws_o);
+  float mx = kNegInf, lsum = 0.f;
+  float acc[16];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int idx = int(threadIdx.x) + f * 256;
-    const int lane = idx & 63, frag = idx >> 6, db = frag >> 2, gi = frag & 3;
-    const int lq = lane & 31, lh = lane >> 5;
-    const int row = rg * kRowsPerWG + w * 32 + lq;
-    if (row >= M) continue;
-    float mm = kNegInf;
-    for (int64_t pq = p_first; pq <= p_last; ++pq) {
-      const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
-      mm = fmaxf(mm, ws_ml[sq * kRowsPerWG + w * 32 + lq].x);
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int64_t pq = p_first; pq <= p_last; ++pq) {
+    const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
+    const float2 ml = ws_ml[sq * kRowsPerWG + w * 32 + lq];
+    const int64_t f = (sq * (kRowsPerWG * HD / 8)) + ((w * 4 + db) * 64 + lane) * 2;
+    const uint4 x0 = wo[f], x1 = wo[f + 1];
+    if (ml.x > mx) {
+      const float c = fast_exp2(mx - ml.x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] *= c;
+      lsum *= c;
+      mx = ml.x;
     }
-    float lsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t pq = p_first; pq <= p_last; ++pq) {
-      const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
-      const float2 ml = ws_ml[sq * kRowsPerWG + w * 32 + lq];
-      const float wgt = fast_exp2(ml.x - mm);
-      lsum += wgt * ml.y;
-      const float4 v = wo[sq * (kRowsPerWG * HD / 4) + ((w * 4 + db) * 4 + gi) * 64 + lane];
-      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    const float wgt = ml.y * fast_exp2(ml.x - mx);
+    lsum += wgt;
+    const uint32_t h[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[2 * i] += wgt * __uint_as_float(h[i] << 16);
+      acc[2 * i + 1] += wgt * __uint_as_float(h[i] & 0xffff0000u);
     }
-    const float inv = 1.0f / lsum;
-    const int s = row / G, jh = row - (row / G) * G;
-    bf16x4 o4;
-    o4[0] = bf16(acc.x * inv); o4[1] = bf16(acc.y * inv); o4[2] = bf16(acc.z * inv); o4[3] = bf16(acc.w * inv);
-    *reinterpret_cast<bf16x4 *>(out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + jh) * HD +
-                                db * 32 + gi * 8 + lh * 4) = o4;
   }
+  const float inv = 1.0f / lsum;
+  const int s = row / G, jh = row - (row / G) * G;
+  bf16 *dst = out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + jh) * HD + db * 32 + lh * 4;
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi)
+    *reinterpret_cast<uint2 *>(dst + gi * 8) =
+        make_uint2(pack_bf16(acc[gi * 4] * inv, acc[gi * 4 + 1] * inv),
+                   pack_bf16(acc[gi * 4 + 2] * inv, acc[gi * 4 + 3] * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -629,7 +650,7 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
     char *wsb = static_cast<char *>(ws);
     int64_t *prefix = reinterpret_cast<int64_t *>(wsb + p.off_prefix);
     float2 *ws_ml = reinterpret_cast<float2 *>(wsb + p.off_ml);
-    float *ws_o = reinterpret_cast<float *>(wsb + p.off_o);
+    bf16 *ws_o = reinterpret_cast<bf16 *>(wsb + p.off_o);
     hipLaunchKernelGGL(attn_bf16_mfma, dim3(p.grid), dim3(kWGThreads), 0, st,
                        static_cast<const bf16 *>(a->q), static_cast<const bf16 *>(a->k_blk),
                        static_cast<const bf16 *>(a->v_blk), static_cast<const bf16 *>(a->k_ctx),

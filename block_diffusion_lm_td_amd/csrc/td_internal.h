@@ -27,7 +27,7 @@ struct AttnPlan {
   // workspace pieces (byte offsets), MFMA path
   size_t off_prefix;    // int64 [B+1]: tile prefix over sequences (for the merge)
   size_t off_ml;        // float2 [2*grid][256]: partial (m, l)
-  size_t off_o;         // float [2*grid][256*128]: partial O
+  size_t off_o;         // bf16 [2*grid][256*128]: partial O / l
   size_t ws_bytes;      // total
   float scale_log2;     // scale * log2(e)
 };

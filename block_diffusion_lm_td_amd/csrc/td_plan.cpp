@@ -68,7 +68,7 @@ AttnPlan plan_attn(const td_attn_args *a) {
     size_t o = 0;
     p.off_prefix = o; o += align256(size_t(a->B + 1) * 8);
     p.off_ml = o;     o += align256(size_t(2) * p.grid * kRowsPerWG * 8);
-    p.off_o = o;      o += align256(size_t(2) * p.grid * kRowsPerWG * 128 * 4);
+    p.off_o = o;      o += align256(size_t(2) * p.grid * kRowsPerWG * 128 * 2);
     p.ws_bytes = o;
   } else {
     p.row_groups = (p.M + 63) / 64;

@@ -78,10 +78,10 @@ def test_attn_empty_context_needs_no_context_pointers(L):
 
 def test_attn_workspace_bytes(L):
     """bf16 / D=128 (MFMA path): a persistent grid of 256 workgroups, each
-    with two fp32 partial slots (256 x 128 O values + 256 (m, l) pairs),
+    with two partial slots (256 x 128 bf16 O / l values + 256 fp32 (m, l) pairs),
     plus per-sequence, per-workgroup and per-unit tables.  The size depends
     on the batch shape only, never on the context lengths."""
-    slot = 256 * 128 * 4 + 256 * 8
+    slot = 256 * 128 * 2 + 256 * 8
     for B, Lmax, S, Hq in [(64, 8192, 16, 32), (4, 65536, 16, 32), (8, 4096, 16, 32),
                            (32, 2048, 64, 32), (3, 1000, 1, 32)]:
         a = attn(B=B, S=S, Hq=Hq, total_ctx=B * Lmax, max_ctx=Lmax)

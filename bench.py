@@ -102,7 +102,19 @@ def cpu_baseline(w, a, c, el, budget_s):
             "sample": f"{n} of {w.B} sequences (attention of all 32 heads + commit of all "
                       f"{w.S} positions), {t_attn + t_commit:.1f} s of fp64 numpy; scaled to the "
                       f"batch by context keys (attention) and sequence count (commit)",
-            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

@@ -97,6 +97,14 @@ __device__ inline void dma16(const void *src, uint32_t lds_base) {
                : "s"(lds_base), "v"(src)
                : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset:
+// no per-lane address arithmetic.
+__device__ inline void dma16s(const void *base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 1"
+               :
+               : "s"(lds_base), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
 __device__ inline uint32_t lds_addr(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
 }
@@ -189,9 +197,12 @@ __device__ __forceinline__ void scale_p(bf16x8 (&p)[2], float alpha) {
 }
 // row max of a half (both lane halves hold the same query), in the exp2 domain
 __device__ __forceinline__ float max_half(const f32x16 &s, float sl2) {
-  float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  a = fmaxf(fmaxf(a, b), c);
+  d = fmaxf(fmaxf(d, e), s[15]);
+  const float mx = fmaxf(a, d);
   return fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
 }
 // keys h*32 + key >= nvalid get a score of -inf
@@ -292,42 +303,50 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int64_t kvs = int64_t(Hkv) * HD;
 
-  // ---- DMA issue of one tile: K and V rows w*8 .. w*8+7, two 4-row (1 KB) pieces each
+  // ---- DMA issue of one tile: K and V rows w*8 .. w*8+7, two 4-row (1 KB)
+  // pieces each; lane i fills LDS slot i%16 of row w*8 + r*4 + i/16
+  uint32_t dko[2], dvo[2];       // lane byte offsets inside a tile of the context cache
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int R = w * 8 + r * 4 + (lane >> 4), cs = lane & 15;
+    dko[r] = uint32_t(R) * uint32_t(kvs) * 2u + uint32_t(cs ^ (R & 15)) * 16u;
+    dvo[r] = uint32_t(R) * uint32_t(kvs) * 2u + uint32_t(cs ^ ((R & 3) << 2)) * 16u;
+  }
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_addr(Ks + (w * 8) * HD));
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane(lds_addr(Vs + (w * 8) * HD));
   auto issue = [&](const Cur &c, int stage) {
     const int g = c.uis / RG;
     const int k0 = c.j * T;
+    const uint32_t lk = lds_k + uint32_t(stage) * (TE * 2), lv = lds_v + uint32_t(stage) * (TE * 2);
+    if (k0 + T <= c.L) {                       // whole tile in the context cache
+      const int64_t e0 = (c.lo + k0) * kvs + int64_t(g) * HD;
+      dma16s(kc + e0, dko[0], lk);
+      dma16s(vc + e0, dvo[0], lv);
+      dma16s(kc + e0, dko[1], lk + 4 * HD * 2);
+      dma16s(vc + e0, dvo[1], lv + 4 * HD * 2);
+      return;
+    }
+    // the tile reaches into the block's own keys (or past their end)
     const int nvalid = min(T, c.L + S - k0);
     const bf16 *kcg = kc + c.lo * kvs + int64_t(g) * HD;
     const bf16 *vcg = vc + c.lo * kvs + int64_t(g) * HD;
     const bf16 *kbg = kb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
     const bf16 *vbg = vb + int64_t(c.b) * S * kvs + int64_t(g) * HD;
-    const bool fast = k0 + T <= c.L;               // whole tile in the context cache
-    const int64_t fbase = (c.lo + k0) * kvs + int64_t(g) * HD;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int R = w * 8 + r * 4 + (lane >> 4);        // tile row (key)
-      const int cs = lane & 15;                          // LDS chunk slot
-      const int ck = cs ^ (R & 15);
-      const int cv = cs ^ ((R & 3) << 2);
-      const bf16 *ksrc, *vsrc;
-      if (fast) {
-        ksrc = kc + fbase + int64_t(R) * kvs + ck * 8;
-        vsrc = vc + fbase + int64_t(R) * kvs + cv * 8;
-      } else {
-        const int key = k0 + (R < nvalid ? R : 0);       // rows past the end re-read a valid key
-        const int64_t roff = int64_t(key < c.L ? key : key - c.L) * kvs;
-        ksrc = (key < c.L ? kcg : kbg) + roff + ck * 8;
-        vsrc = (key < c.L ? vcg : vbg) + roff + cv * 8;
-      }
-      const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_addr(Ks + stage * TE + (w * 8 + r * 4) * HD));
-      const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_addr(Vs + stage * TE + (w * 8 + r * 4) * HD));
-      dma16(ksrc, kl);
-      dma16(vsrc, vl);
+      const int R = w * 8 + r * 4 + (lane >> 4);
+      const int cs = lane & 15;
+      const int key = k0 + (R < nvalid ? R : 0);           // rows past the end re-read a valid key
+      const int64_t roff = int64_t(key < c.L ? key : key - c.L) * kvs;
+      dma16((key < c.L ? kcg : kbg) + roff + (cs ^ (R & 15)) * 8, lk + r * 4 * HD * 2);
+      dma16((key < c.L ? vcg : vbg) + roff + (cs ^ ((R & 3) << 2)) * 8, lv + r * 4 * HD * 2);
     }
   };
 
   Cur ld, cc;
-  ld.b = s_loc[0]; ld.uis = s_loc[1]; ld.j = s_loc[2];
+  ld.b = __builtin_amdgcn_readfirstlane(s_loc[0]);
+  ld.uis = __builtin_amdgcn_readfirstlane(s_loc[1]);
+  ld.j = __builtin_amdgcn_readfirstlane(s_loc[2]);
   cur_load(ld, off, total_ctx, max_ctx, S);
   cc = ld;
   for (int x = 0; x < 2 && t_begin + x < t_end; ++x) {

@@ -369,18 +369,36 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   // Moves the running max when the half's max exceeds it by more than 2^8
   // (lazy rescale: exact in real arithmetic, keeps P <= 256).  O must hold
   // exactly the products made with the old max when this runs.
-  auto lazy = [&](float mxs, float &alpha) -> bool {
+  // The rescale is rare after a sequence's first tiles; the empty volatile
+  // asm keeps it behind a real branch (the compiler would otherwise
+  // if-convert it and pay the 64 multiplies on every tile).
+  auto lazy = [&](float mxs, float &alpha, bool with_pb) {
     const bool need = mxs > m + kLazy;
     if (__any(need)) {
+      asm volatile("");
       const float mn = need ? mxs : m;
       alpha = fast_exp2(m - mn);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       l *= alpha;
       m = mn;
-      return true;
+      if (with_pb) scale_p(pB, alpha);       // a pending P made with the old max
     }
-    return false;
+  };
+
+  // Softmax of a half of a full tile against the running max, without first
+  // taking the half's max: every P <= 256 as long as no lane's sum exceeds
+  // 256; if one does, the half's max is taken, O and l are rescaled (lazy:
+  // only if the max grew by more than 2^8) and P is recomputed.
+  auto guarded_sm = [&](const f32x16 &sX, bf16x8 (&pX)[2]) -> float {
+    float sum = sm_half(sX, m, sl2, pX);
+    if (__any(!(sum <= 256.f))) {
+      asm volatile("");
+      float alpha;
+      lazy(max_half(sX, sl2), alpha, false);
+      sum = sm_half(sX, m, sl2, pX);
+    }
+    return sum;
   };
 
   // Per tile t (halves A = keys 0-31, B = keys 32-63), three phases whose
@@ -442,7 +460,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       const bf16 *Vt = Vs + st * TE;
       qk_half(Kt, 0, lq, lh, qf, sA);
       if (nvalid < 32) mask_half(sA, 0, lh, nvalid);
-      lazy(max_half(sA, sl2), alpha);
+      lazy(max_half(sA, sl2), alpha, false);
       qk_half(Kt, 1, lq, lh, qf, sB);
       l += sm_half(sA, m, sl2, pA);
       pv_half(Vt, 0, e4, v_lane_off, pA, o);
@@ -454,17 +472,15 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       const bf16 *Kt = Ks + st * TE;
       const bf16 *Vt = Vs + st * TE;
       const bf16 *Vp = Vs + ((st + NST - 1) & (NST - 1)) * TE;
-      lazy(max_half(sB, sl2), alpha);
       // phase 1
       qk_half(Kt, 0, lq, lh, qf, sA);
-      l += sm_half(sB, m, sl2, pB);
+      l += guarded_sm(sB, pB);
       if (may_mask && nvalid < 32) mask_half(sA, 0, lh, nvalid);
-      // the pending P_B was made with the old max
-      if (lazy(max_half(sA, sl2), alpha)) scale_p(pB, alpha);
-      // phases 2 and 3
+      // phases 2 and 3 (PV_B(t-1) is issued before A's guard, so a rescale
+      // there sees O complete up to B(t-1))
       qk_half(Kt, 1, lq, lh, qf, sB);
       pv_half(Vp, 1, e4, v_lane_off, pB, o);
-      l += sm_half(sA, m, sl2, pA);
+      l += guarded_sm(sA, pA);
       pv_half(Vt, 0, e4, v_lane_off, pA, o);
     };
     auto advance = [&]() {
@@ -483,7 +499,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       const int stl = (st + NST - 1) & (NST - 1);
       const bf16 *Vl = Vs + stl * TE;
       if (nvalid < T) mask_half(sB, 1, lh, nvalid);
-      lazy(max_half(sB, sl2), alpha);
+      lazy(max_half(sB, sl2), alpha, false);
       l += sm_half(sB, m, sl2, pB);
       pv_half(Vl, 1, e4, v_lane_off, pB, o);
     }

@@ -51,15 +51,16 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the attention kernel from committed rocprofv3
-    counter runs, valid only while the kernel source is unchanged."""
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernels from committed rocprofv3
+    counter runs on this workload, valid only while the kernel source is
+    unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(ATTN_SRC):
+    if t.get("source_sha") != source_sha(ATTN_SRC) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -117,6 +118,98 @@ def cpu_model():
     return None
 
 
+def block_loop(args, L):
+    """The full block-denoising loop on the loop workload: for each (S, gamma),
+    td_denoise_step repeats until no position is masked.  Per-step logits come
+    from the seeded loop generator (only each row's peak logit changes between
+    steps; the update runs between the timed steps).  Reports steps per block
+    and committed tokens/s over the timed steps."""
+    import numpy as np
+    import torch
+    import block_diffusion_lm_td_amd as td
+    from block_diffusion_lm_td_amd import _td
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for S in (16, 32, 64):
+        w0 = synth.WORKLOADS["bf16_b32_ctx2k_loop"].with_(S=S)
+        a = synth.make_attention_inputs(w0, args.seed + S)
+        att = {k: up(a[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx")}
+        off = torch.from_numpy(a["offsets"]).to(dev)
+        out = torch.empty_like(att["q"])
+        for gamma in (0.5, 0.8, 0.95):
+            w = w0.with_(gamma=gamma)
+            log(f"[loop] S={S} gamma={gamma}: generating logits")
+            base, peak, stored = synth.loop_peak_values(w, args.seed + 100 * S, S + 1)
+            logits = up(base).view(w.B, w.S, w.V)
+            rows = torch.arange(w.B * w.S, device=dev)
+            peak_d = torch.from_numpy(peak).to(dev)
+            stored_d = up(stored)
+            B = w.B
+            o = dict(commit=torch.empty((B, S), dtype=torch.uint8, device=dev),
+                     token=torch.empty((B, S), dtype=torch.int32, device=dev),
+                     maxprob=torch.empty((B, S), dtype=torch.float32, device=dev),
+                     n_commit=torch.empty((B,), dtype=torch.int32, device=dev),
+                     masked_in=torch.ones((B, S), dtype=torch.uint8, device=dev),
+                     masked_out=torch.empty((B, S), dtype=torch.uint8, device=dev),
+                     tokens=torch.full((B, S), -1, dtype=torch.int32, device=dev),
+                     n_left=torch.empty((1,), dtype=torch.int32, device=dev))
+            aa = td.attn_args(att["q"], att["k_blk"], att["v_blk"], att["k_ctx"], att["v_ctx"], off, out,
+                              a["total_ctx"], a["max_ctx"])
+            cc = td.commit_args(logits, o["commit"], o["token"], gamma, o["masked_in"], o["maxprob"],
+                                o["n_commit"], o["masked_out"], o["tokens"], o["n_left"])
+            need = L.td_denoise_workspace_bytes(ctypes.byref(aa), ctypes.byref(cc))
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            wsp = ctypes.c_void_p(ws.data_ptr())
+
+            def run_block(timed):
+                o["masked_in"].fill_(1)
+                o["tokens"].fill_(-1)
+                done_at = np.zeros(B, np.int64)
+                ms = 0.0
+                steps = 0
+                while True:
+                    logits.view(-1, w.V)[rows, peak_d] = stored_d[steps]
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    r = L.td_denoise_step(ctypes.byref(aa), ctypes.byref(cc), wsp, ws.numel(), sp)
+                    e1.record(stream)
+                    if r != 0:
+                        raise RuntimeError(_td.status_str(r))
+                    torch.cuda.synchronize()
+                    ms += e0.elapsed_time(e1)
+                    steps += 1
+                    left = o["masked_out"].view(B, S).sum(dim=1).cpu().numpy()
+                    done_at[(left == 0) & (done_at == 0)] = steps
+                    if int(o["n_left"].item()) == 0:
+                        break
+                    if steps >= S:
+                        raise RuntimeError("a block did not finish within S steps")
+                    o["masked_in"].copy_(o["masked_out"])
+                return steps, done_at, ms
+
+            run_block(False)                       # warm-up pass
+            steps, done_at, ms = run_block(True)
+            committed = B * S
+            print(json.dumps({
+                "metric": "block loop: steps per block and committed tokens/s",
+                "workload": w.name, "B": B, "S": S, "gamma": gamma, "ctx_len": w.ctx_lo, "V": w.V,
+                "dtype": w.dtype, "data": "synthetic",
+                "loop_steps": steps, "steps_per_block_mean": round(float(done_at.mean()), 3),
+                "steps_per_block_max": int(done_at.max()),
+                "ms_total": round(ms, 4), "ms_per_step": round(ms / steps, 5),
+                "committed_tokens_per_s": round(committed / (ms * 1e-3), 1)}), flush=True)
+            del logits, stored_d, ws
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +222,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
+    ap.add_argument("--loop", action="store_true",
+                    help="block loop: S in {16,32,64} x gamma in {0.5,0.8,0.95}, steps until every "
+                         "position is committed (one JSON line per case)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,6 +241,9 @@ def main():
     import synth
 
     L = td.lib()
+    if args.loop:
+        block_loop(args, L)
+        return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -243,7 +342,7 @@ def main():
 
     attn_bytes, attn_flops, commit_bytes = algorithmic(w, a["lengths"])
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name)
     steps_per_s = 1e3 / ms_per_step
     res = {
         "metric": METRIC,

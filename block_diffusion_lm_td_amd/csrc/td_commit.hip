@@ -110,8 +110,13 @@ __global__ __launch_bounds__(256) void commit_rows(const T *__restrict__ logits,
       absorb<1>(f, e, m, z, bv);
     }
   }
-  // lowest index of the lane's max
+  // lowest index of the lane's max; only lanes holding their wave's max can
+  // hold the row's argmax, so only they re-read their best vector
   int idx = kNoIndex;
+  float wmx = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wmx = fmaxf(wmx, __shfl_xor(wmx, o));
+  if (m < wmx) bv = -1;
   if (bv >= 0) {
     if (VEC) {
       float f[NV];

@@ -230,7 +230,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the denoise step of one attention layer is one "
               "GPU's share (sequences shard over GPUs with no exchange); --gpus above 1 is not "
-              "supported by this build", file=sys.stderr)
+              "supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

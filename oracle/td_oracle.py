@@ -19,7 +19,7 @@ Sources (the pages are news articles on NVIDIA's Nemotron-Labs-TwoTower):
   [aikraft]   aikraft.ru, architecture section: the denoiser cross-attends to
               the context tower's layers; results section: gamma, S.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * block attention and the layer-aligned cross-attention are ONE softmax over
     the keys [context ; block] -- the only reading under which an empty
     context gives plain bidirectional block attention and S = 1 gives causal

@@ -1,7 +1,7 @@
 """Helpers of the GPU parity tests: upload seeded inputs, run the C ABI
 through the binding, compare with the oracle.
 
-Gates (stated in the tests' docstrings, derived in the design doc):
+Gates (also stated in the tests' docstrings):
   attention, bf16 inputs: max abs err <= 2e-2, mean abs err <= 2e-3 versus
     float64, plus relative L2 error <= 1e-2 (the absolute gates are loose
     for inputs scaled by 1/sqrt(128), whose outputs are ~1e-3);

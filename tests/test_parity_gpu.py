@@ -101,6 +101,27 @@ def test_attn_b64_ragged_sampled_and_deterministic():
     assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
 
 
+def test_attn_many_sequences_sampled():
+    """More sequences than the workgroup has threads: the prologue scans the
+    ragged lengths in several passes; many short (and empty) contexts."""
+    w = W["bf16_b8_ctx4k"].with_(B=600)
+    lengths = np.random.default_rng(31).integers(0, 120, size=600)
+    lengths[[5, 77, 599]] = 0
+    a = synth.make_attention_inputs(w, 31, lengths=lengths)
+    log("case attn B=600 short contexts")
+    got = run_attn(upload_attn(a), a)
+    seqs = [0, 5, 77, 255, 511, 512, 513, 598, 599]
+    check_attn(got[seqs], oracle_attn(a, seqs), f"B=600 sampled seqs={seqs}")
+
+
+def test_attn_b64_ctx8k_sampled():
+    w = W["bf16_b64_ctx8k"]
+    a = synth.make_attention_inputs(w, 1006)
+    log("case attn b64 ctx8k sampled")
+    got = run_attn(upload_attn(a), a)
+    check_attn(got[[0, 40, 63]], oracle_attn(a, [0, 40, 63]), "b64 ctx8k seqs 0,40,63")
+
+
 def test_attn_b4_ctx64k_sampled():
     w = W["bf16_b4_ctx64k"]
     a = synth.make_attention_inputs(w, 1004)

@@ -20,7 +20,9 @@
 // reads.  The key order inside each 16-key step is permuted identically on
 // both operands.  Softmax runs in the exp2 domain with a lazy rescale: the
 // running max only moves when a tile's max exceeds it by more than 2^8,
-// which is exact in real arithmetic and keeps P <= 256.
+// which is exact in real arithmetic and keeps P <= 256.  Full tiles skip the
+// max altogether: P is computed against the running max and the max is only
+// taken (and O rescaled) when a lane's sum of P exceeds 256.
 //
 // Any other dtype / head dim: attn_valu, one thread per query row (a plain
 // correctness path for small fp32 problems).

@@ -73,7 +73,8 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
 // ceil((L_b + S) / 64) key tiles of its sequence, and all units' tiles form
 // one global sequence of W tiles.  Each of the Pe = min(P, W) persistent
 // workgroups scans the ragged lengths itself (in LDS, no separate planning
-// launch) and walks an equal contiguous range of that sequence.  Units a
+// launch) and walks a contiguous range of that sequence, the ranges being
+// equal in cost (tiles plus a fixed charge per unit started).  Units a
 // workgroup covers whole are normalised and written directly; where a range
 // cuts a unit, the workgroup writes a partial (O / l in bf16, m, l) into one of its
 // two slots, and attn_merge combines the partials of every cut unit after
@@ -117,12 +118,22 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
   return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
 }
 
-__device__ inline int64_t wg_begin(int64_t p, int64_t W, int P) { return p * W / P; }
-// logical workgroup whose range holds global tile t
-__device__ inline int64_t tile_owner(int64_t t, int64_t W, int P) { return ((t + 1) * P - 1) / W; }
-// partial slot of workgroup pq holding its piece of a unit that starts at tile s_u
-__device__ inline int64_t piece_slot(int64_t pq, int64_t p_first, int64_t s_u, int64_t W, int P) {
-  return 2 * pq + ((pq == p_first && s_u != wg_begin(pq, W, P)) ? 1 : 0);
+// Work split.  Starting a unit inside a workgroup's range costs about as much
+// as kSegCost key tiles (the new Q, the pipeline fill and drain, the output),
+// so the split is even in cost, not in tiles: unit (b, g) occupies the cost
+// slots [Cu, Cu + kSegCost + n_b) of a global cost axis, its n_b tiles being
+// the last n_b of them, with Cu = UPS*(prefix_b + kSegCost*b) + g*(n_b + kSegCost)
+// (prefix_b = tiles of the sequences before b, UPS units per sequence).
+// Logical workgroup p owns the slots [X_p, X_{p+1}), X_p = p*C/P, and with them
+// a contiguous (possibly empty) range of the global tile sequence.
+constexpr int kSegCost = 4;
+__device__ inline int64_t cost_begin(int64_t p, int64_t C, int P) { return p * C / P; }
+// logical workgroup whose cost range holds slot y
+__device__ inline int64_t slot_owner(int64_t y, int64_t C, int P) { return ((y + 1) * P - 1) / C; }
+// partial slot of workgroup pq holding its piece of the unit whose cost range
+// starts at Cu: pq's second slot when pq's range also holds the previous unit
+__device__ inline int64_t piece_slot(int64_t pq, int64_t p_first, int64_t Cu, int64_t C, int P) {
+  return 2 * pq + ((pq == p_first && cost_begin(pq, C, P) < Cu) ? 1 : 0);
 }
 
 struct Cur {
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NST * TE];
   __shared__ int64_t s_scan[kWGThreads];
   __shared__ int s_loc[3];
+  __shared__ int64_t s_t[2];
 
   const int UPS = Hkv * RG;
   const int tid = threadIdx.x;
@@ -269,16 +281,29 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   const int64_t W = wseq * UPS;
   const int Pe = int(W < P ? W : P);          // logical workgroups with work
   if (pid >= Pe) return;
-  const int64_t t_begin = wg_begin(pid, W, Pe), t_end = wg_begin(pid + 1, W, Pe);
+  const int64_t C = UPS * (wseq + int64_t(kSegCost) * B);
+  const int64_t X0 = cost_begin(pid, C, Pe), X1 = cost_begin(pid + 1, C, Pe);
+  // the first tile at or after cost slot X of sequence b (excl tiles before it, n per unit)
+  auto locate = [&](int64_t X, int b, int64_t excl, int64_t n, int k) {
+    const int64_t ce = UPS * (excl + int64_t(kSegCost) * b);
+    const int64_t ci = ce + UPS * (n + kSegCost);
+    if (ce <= X && X < ci) {
+      const int64_t r = X - ce, uc = n + kSegCost;
+      const int64_t u = r / uc, rr = r - u * uc;
+      const int64_t j = rr > kSegCost ? rr - kSegCost : 0;
+      s_t[k] = excl * UPS + u * n + j;
+      if (k == 0) { s_loc[0] = b; s_loc[1] = int(u); s_loc[2] = int(j); }
+    }
+  };
+  if (tid == 0) { s_t[0] = W; s_t[1] = W; }   // slots at or past C: the end
+  __syncthreads();
   if (pid == 0 && tid == 0) prefix_out[0] = 0;
   if (one_pass) {
     const int64_t incl = s_scan[tid], excl = incl - n_mine;
     if (tid < B) {
       if (pid == 0) prefix_out[tid + 1] = incl;
-      if (excl * UPS <= t_begin && t_begin < incl * UPS) {
-        const int64_t r = t_begin - excl * UPS;
-        s_loc[0] = tid; s_loc[1] = int(r / n_mine); s_loc[2] = int(r - (r / n_mine) * n_mine);
-      }
+      locate(X0, tid, excl, n_mine, 0);
+      locate(X1, tid, excl, n_mine, 1);
     }
   } else {
     int64_t running = 0;
@@ -291,16 +316,16 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       const int64_t incl = running + s_scan[tid], excl = incl - n;
       if (b < B) {
         if (pid == 0) prefix_out[b + 1] = incl;
-        if (excl * UPS <= t_begin && t_begin < incl * UPS) {
-          const int64_t r = t_begin - excl * UPS;
-          s_loc[0] = b; s_loc[1] = int(r / n); s_loc[2] = int(r - (r / n) * n);
-        }
+        locate(X0, b, excl, n, 0);
+        locate(X1, b, excl, n, 1);
       }
       running += s_scan[kWGThreads - 1];
       __syncthreads();
     }
   }
   __syncthreads();
+  const int64_t t_begin = s_t[0], t_end = s_t[1];
+  if (t_begin >= t_end) return;                // a range of overhead slots only
 
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int64_t kvs = int64_t(Hkv) * HD;
@@ -556,9 +581,11 @@ __global__ __launch_bounds__(256) void attn_merge(
   const int g = uis / RG, rg = uis - (uis / RG) * RG;
   const int64_t W = prefix[B] * UPS;
   const int Pe = int(W < P ? W : P);
+  const int64_t C = UPS * (prefix[B] + int64_t(kSegCost) * B);
   const int64_t n = prefix[b + 1] - prefix[b];
-  const int64_t s_u = prefix[b] * UPS + int64_t(uis) * n, e_u = s_u + n;
-  const int64_t p_first = tile_owner(s_u, W, Pe), p_last = tile_owner(e_u - 1, W, Pe);
+  const int64_t Cu = UPS * (prefix[b] + int64_t(kSegCost) * b) + int64_t(uis) * (n + kSegCost);
+  const int64_t y0 = Cu + kSegCost;               // cost slots of the unit's first and last tiles
+  const int64_t p_first = slot_owner(y0, C, Pe), p_last = slot_owner(y0 + n - 1, C, Pe);
   if (p_first == p_last) return;                 // written whole by its workgroup
   const int lane = threadIdx.x & 63, db = threadIdx.x >> 6;
   const int lq = lane & 31, lh = lane >> 5;
@@ -570,7 +597,7 @@ __global__ __launch_bounds__(256) void attn_merge(
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   for (int64_t pq = p_first; pq <= p_last; ++pq) {
-    const int64_t sq = piece_slot(pq, p_first, s_u, W, Pe);
+    const int64_t sq = piece_slot(pq, p_first, Cu, C, Pe);
     const float2 ml = ws_ml[sq * kRowsPerWG + w * 32 + lq];
     const int64_t f = (sq * (kRowsPerWG * HD / 8)) + ((w * 4 + db) * 64 + lane) * 2;
     const uint4 x0 = wo[f], x1 = wo[f + 1];

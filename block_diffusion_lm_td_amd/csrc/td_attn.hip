@@ -201,13 +201,6 @@ __device__ __forceinline__ void pv_half(const bf16 *__restrict__ Vt, int h, int 
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[db], 0, 0, 0);
     }
 }
-// P *= alpha in place (bf16), used when the running max moves while P waits
-__device__ __forceinline__ void scale_p(bf16x8 (&p)[2], float alpha) {
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[kk][i] = bf16(float(p[kk][i]) * alpha);
-}
 // row max of a half (both lane halves hold the same query), in the exp2 domain
 __device__ __forceinline__ float max_half(const f32x16 &s, float sl2) {
   float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
@@ -217,6 +210,57 @@ __device__ __forceinline__ float max_half(const f32x16 &s, float sl2) {
   d = fmaxf(fmaxf(d, e), s[15]);
   const float mx = fmaxf(a, d);
   return fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+}
+// One pipeline step in a fixed instruction order: QK for keys hq*32.. of the
+// K tile Kq into sq (8 MFMAs, one dependent chain), PV for keys hv*32.. of
+// the V tile Vv with P = pv (8 MFMAs, four chains), and the softmax of the
+// scores ss into ps.  Slot i issues one MFMA (QK and PV alternating, so the
+// QK chain never stalls on itself), the softmax of score i, and the LDS reads
+// of the operands for slot i + kAhead; the scheduling fences keep that order,
+// so each wave keeps the matrix core and the VALU busy at once.  Returns the
+// lane's sum of its 16 P values.
+constexpr int kAhead = 2;
+__device__ __forceinline__ float step16(const bf16 *__restrict__ Kq, int hq, const bf16 *__restrict__ Vv,
+                                        int hv, int lq, int lh, int e4, int v_lane_off,
+                                        const bf16x8 (&qf)[8], f32x16 &sq, const bf16x8 (&pv)[2],
+                                        f32x16 (&o)[4], const f32x16 &ss, float m, float sl2,
+                                        bf16x8 (&ps)[2]) {
+  const int row = hq * 32 + lq;
+  bf16x8 opnd[16];
+  auto load = [&](int i) {
+    if ((i & 1) == 0) {
+      const int ks = i >> 1;
+      opnd[i] = *reinterpret_cast<const bf16x8 *>(Kq + row * HD + (((ks * 2 + lh) ^ (row & 15)) * 8));
+    } else {
+      const int kk = (i >> 1) >> 2, db = (i >> 1) & 3;
+      const bf16 *base = Vv + (hv * 2 + kk) * 16 * HD + v_lane_off + ((db ^ e4) * 32);
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base));
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + 8 * HD));
+      const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+      const u32x4 a01 = {a0.x, a0.y, a1.x, a1.y};
+      opnd[i] = __builtin_bit_cast(bf16x8, a01);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) load(i);
+  float acc = 0.f;
+  sq = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if ((i & 1) == 0) {
+      sq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], qf[i >> 1], sq, 0, 0, 0);
+    } else {
+      const int kk = (i >> 1) >> 2, db = (i >> 1) & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], pv[kk], o[db], 0, 0, 0);
+    }
+    const float pe = fast_exp2(__builtin_fmaf(ss[i], sl2, -m));
+    acc += pe;
+    ps[i >> 3][i & 7] = bf16(pe);
+    if (i + kAhead < 16) load(i + kAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return acc;
 }
 // keys h*32 + key >= nvalid get a score of -inf
 __device__ __forceinline__ void mask_half(f32x16 &s, int h, int lh, int nvalid) {
@@ -399,42 +443,46 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   // The rescale is rare after a sequence's first tiles; the empty volatile
   // asm keeps it behind a real branch (the compiler would otherwise
   // if-convert it and pay the 64 multiplies on every tile).
-  auto lazy = [&](float mxs, float &alpha, bool with_pb) {
+  auto lazy = [&](float mxs) {
     const bool need = mxs > m + kLazy;
     if (__any(need)) {
       asm volatile("");
       const float mn = need ? mxs : m;
-      alpha = fast_exp2(m - mn);
+      const float alpha = fast_exp2(m - mn);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       l *= alpha;
       m = mn;
-      if (with_pb) scale_p(pB, alpha);       // a pending P made with the old max
     }
   };
 
   // Softmax of a half of a full tile against the running max, without first
   // taking the half's max: every P <= 256 as long as no lane's sum exceeds
-  // 256; if one does, the half's max is taken, O and l are rescaled (lazy:
-  // only if the max grew by more than 2^8) and P is recomputed.
-  auto guarded_sm = [&](const f32x16 &sX, bf16x8 (&pX)[2]) -> float {
-    float sum = sm_half(sX, m, sl2, pX);
+  // 256; if one does, the half's scores are recomputed from the K tile
+  // (still in LDS) and masked as before, the half's max is taken, O and l
+  // are rescaled (lazy: only if the max grew by more than 2^8) and P is
+  // recomputed.  Recomputing the scores on that rare path, rather than
+  // keeping them, frees their registers once P is formed.
+  auto guard = [&](float sum, bf16x8 (&pX)[2], const bf16 *Kx, int hx, int nv) -> float {
     if (__any(!(sum <= 256.f))) {
       asm volatile("");
-      float alpha;
-      lazy(max_half(sX, sl2), alpha, false);
-      sum = sm_half(sX, m, sl2, pX);
+      f32x16 sR;
+      qk_half(Kx, hx, lq, lh, qf, sR);
+      if (nv < 32 * (hx + 1)) mask_half(sR, hx, lh, nv);
+      lazy(max_half(sR, sl2));
+      sum = sm_half(sR, m, sl2, pX);
     }
     return sum;
   };
 
-  // Per tile t (halves A = keys 0-31, B = keys 32-63), three phases whose
-  // matrix work and softmax work are independent:
-  //   1: QK_A(t)                 || softmax B(t-1)
+  // Per tile t (halves A = keys 0-31, B = keys 32-63), two steps of 16
+  // MFMAs each, whose matrix work and softmax work are independent:
+  //   1: QK_A(t) + PV_A(t-1)     || softmax B(t-1)
   //   2: QK_B(t) + PV_B(t-1)     || softmax A(t)
-  //   3: PV_A(t)
-  // A segment's first tile has no B(t-1); the B half of its last tile is
-  // finished right after that tile's phase 3.  Each phase is one basic block.
+  // so a half's scores wait one step for their softmax and its P one more
+  // for the PV product.  A segment's first tile only fills the pipeline
+  // (QK of both halves, softmax A); its last tile is finished after the loop.
+  // Each step is one basic block up to the softmax guard.
   int64_t t = t_begin;
   int st = 0;
   // wait for tile t (only tile t+1 may still be in flight), publish it, and
@@ -479,36 +527,31 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     l = 0.f;
 
     // first tile of the segment
-    float alpha;
     next_tile();
     int nvalid = min(T, cc.L + S - cc.j * T);
     {
       const bf16 *Kt = Ks + st * TE;
-      const bf16 *Vt = Vs + st * TE;
       qk_half(Kt, 0, lq, lh, qf, sA);
       if (nvalid < 32) mask_half(sA, 0, lh, nvalid);
-      lazy(max_half(sA, sl2), alpha, false);
+      lazy(max_half(sA, sl2));
       qk_half(Kt, 1, lq, lh, qf, sB);
       l += sm_half(sA, m, sl2, pA);
-      pv_half(Vt, 0, e4, v_lane_off, pA, o);
     }
     // steady tiles: all full (only a segment's last tile can be partial)
     auto steady = [&](bool may_mask) {
       next_tile();
       nvalid = min(T, cc.L + S - cc.j * T);
       const bf16 *Kt = Ks + st * TE;
-      const bf16 *Vt = Vs + st * TE;
+      const bf16 *Kp = Ks + ((st + NST - 1) & (NST - 1)) * TE;
       const bf16 *Vp = Vs + ((st + NST - 1) & (NST - 1)) * TE;
-      // phase 1
-      qk_half(Kt, 0, lq, lh, qf, sA);
-      l += guarded_sm(sB, pB);
+      // step 1 (PV_A(t-1) comes before B(t-1)'s guard in program order, so a
+      // rescale there finds O complete up to A(t-1) and no P pending)
+      l += guard(step16(Kt, 0, Vp, 0, lq, lh, e4, v_lane_off, qf, sA, pA, o, sB, m, sl2, pB),
+                 pB, Kp, 1, T);
       if (may_mask && nvalid < 32) mask_half(sA, 0, lh, nvalid);
-      // phases 2 and 3 (PV_B(t-1) is issued before A's guard, so a rescale
-      // there sees O complete up to B(t-1))
-      qk_half(Kt, 1, lq, lh, qf, sB);
-      pv_half(Vp, 1, e4, v_lane_off, pB, o);
-      l += guarded_sm(sA, pA);
-      pv_half(Vt, 0, e4, v_lane_off, pA, o);
+      // step 2
+      l += guard(step16(Kt, 1, Vp, 1, lq, lh, e4, v_lane_off, qf, sB, pB, o, sA, m, sl2, pA),
+                 pA, Kt, 0, may_mask ? nvalid : T);
     };
     auto advance = [&]() {
       ++t;
@@ -521,12 +564,13 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       steady(true);
       advance();
     }
-    // B half of the segment's last tile (stage st - 1), then the output
+    // PV_A and the B half of the segment's last tile (stage st - 1), then the output
     {
       const int stl = (st + NST - 1) & (NST - 1);
       const bf16 *Vl = Vs + stl * TE;
+      pv_half(Vl, 0, e4, v_lane_off, pA, o);
       if (nvalid < T) mask_half(sB, 1, lh, nvalid);
-      lazy(max_half(sB, sl2), alpha, false);
+      lazy(max_half(sB, sl2));
       l += sm_half(sB, m, sl2, pB);
       pv_half(Vl, 1, e4, v_lane_off, pB, o);
     }

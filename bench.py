@@ -225,6 +225,10 @@ def main():
     ap.add_argument("--loop", action="store_true",
                     help="block loop: S in {16,32,64} x gamma in {0.5,0.8,0.95}, steps until every "
                          "position is committed (one JSON line per case)")
+    ap.add_argument("--hold", type=float, default=0.0,
+                    help="run --hold-part back-to-back for this many seconds (for sampling board "
+                         "power and clocks from outside), print one JSON line and exit")
+    ap.add_argument("--hold-part", choices=("step", "attn", "commit"), default="attn")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -299,6 +303,23 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    if args.hold > 0:
+        call = {"step": lambda r: L.td_denoise_step(r[0], r[1], ws_ptr, ws.numel(), sp),
+                "attn": lambda r: L.td_block_attn(r[0], ws_ptr, ws.numel(), sp),
+                "commit": lambda r: L.td_commit(r[1], ws_ptr, ws.numel(), sp)}[args.hold_part]
+        n, t0 = 0, time.time()
+        while time.time() - t0 < args.hold:
+            for i in range(500):
+                r = call(refs[(n + i) % nsets])
+                if r != 0:
+                    raise RuntimeError(_td.status_str(r))
+            torch.cuda.synchronize()
+            n += 500
+        dt = time.time() - t0
+        print(json.dumps({"hold_part": args.hold_part, "workload": w.name, "launches": n,
+                          "seconds": round(dt, 3), "us_per_launch": round(dt / n * 1e6, 2)}), flush=True)
+        return
 
     # ---- timed region: K whole steps
     t_start = torch.cuda.Event(enable_timing=True)

@@ -95,7 +95,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // explicit vmcnt waits before the barrier that publishes a tile).  The asm
 // has no outputs.
 __device__ inline void dma16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 1"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1 nt\n\ts_nop 1"
                :
                : "s"(lds_base), "v"(src)
                : "memory", "m0");
@@ -103,7 +103,7 @@ __device__ inline void dma16(const void *src, uint32_t lds_base) {
 // The same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset:
 // no per-lane address arithmetic.
 __device__ inline void dma16s(const void *base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 1"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1 nt\n\ts_nop 1"
                :
                : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
@@ -281,45 +281,54 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   // K chunk c of key r sits at c ^ (r % 16), V chunk c at c ^ 4*(r % 4).
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NST * TE];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NST * TE];
-  __shared__ int64_t s_scan[kWGThreads];
-  __shared__ int s_loc[3];
+  __shared__ int64_t s_wsum[kWaves];
   __shared__ int64_t s_t[2];
+  __shared__ int s_loc[3];
 
   const int UPS = Hkv * RG;
   const int tid = threadIdx.x;
   // consecutive logical ranges land on one XCD (dispatch is round-robin over 8)
   const int pid = (P % 8 == 0) ? int(blockIdx.x % 8) * (P / 8) + int(blockIdx.x / 8) : int(blockIdx.x);
 
-  // ---- ragged plan: tiles per sequence, their prefix, this workgroup's start
+  // ---- ragged plan: tiles per sequence, their prefix, this workgroup's range
   auto ntiles = [&](int b) -> int64_t {
     int64_t lo;
     int L;
     seq_range(off, b, total_ctx, max_ctx, lo, L);
     return (int64_t(L) + S + T - 1) / T;
   };
-  auto block_scan = [&]() {            // inclusive scan of s_scan in place
-    for (int d = 1; d < kWGThreads; d <<= 1) {
-      const int64_t v = tid >= d ? s_scan[tid - d] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
+  // inclusive scan of v over the workgroup's threads: shuffles inside each
+  // wave, then the wave totals through LDS; also returns the grand total
+  auto wg_scan = [&](int64_t v, int64_t &total) -> int64_t {
+    const int ln = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(v, d);
+      if (ln >= d) v += y;
     }
+    if (ln == 63) s_wsum[wv] = v;
+    __syncthreads();
+    int64_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const int64_t x = s_wsum[k];
+      if (k < wv) before += x;
+      total += x;
+    }
+    __syncthreads();                           // s_wsum is reused by the next call
+    return v + before;
   };
   const bool one_pass = B <= kWGThreads;
-  int64_t n_mine = 0, wseq = 0;
+  int64_t n_mine = 0, incl_mine = 0, wseq = 0;
   if (one_pass) {
     n_mine = tid < B ? ntiles(tid) : 0;
-    s_scan[tid] = n_mine;
-    __syncthreads();
-    block_scan();
-    wseq = s_scan[kWGThreads - 1];
+    incl_mine = wg_scan(n_mine, wseq);
   } else {
     for (int base = 0; base < B; base += kWGThreads) {
-      s_scan[tid] = base + tid < B ? ntiles(base + tid) : 0;
-      __syncthreads();
-      block_scan();
-      wseq += s_scan[kWGThreads - 1];
-      __syncthreads();
+      int64_t tot;
+      wg_scan(base + tid < B ? ntiles(base + tid) : 0, tot);
+      wseq += tot;
     }
   }
   const int64_t W = wseq * UPS;
@@ -327,7 +336,9 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   if (pid >= Pe) return;
   const int64_t C = UPS * (wseq + int64_t(kSegCost) * B);
   const int64_t X0 = cost_begin(pid, C, Pe), X1 = cost_begin(pid + 1, C, Pe);
-  // the first tile at or after cost slot X of sequence b (excl tiles before it, n per unit)
+  // the first tile at or after cost slot X of sequence b (excl tiles before it,
+  // n per unit); the sequences' cost ranges tile [0, C), so for X < C exactly
+  // one thread finds it
   auto locate = [&](int64_t X, int b, int64_t excl, int64_t n, int k) {
     const int64_t ce = UPS * (excl + int64_t(kSegCost) * b);
     const int64_t ci = ce + UPS * (n + kSegCost);
@@ -339,13 +350,11 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       if (k == 0) { s_loc[0] = b; s_loc[1] = int(u); s_loc[2] = int(j); }
     }
   };
-  if (tid == 0) { s_t[0] = W; s_t[1] = W; }   // slots at or past C: the end
-  __syncthreads();
   if (pid == 0 && tid == 0) prefix_out[0] = 0;
   if (one_pass) {
-    const int64_t incl = s_scan[tid], excl = incl - n_mine;
     if (tid < B) {
-      if (pid == 0) prefix_out[tid + 1] = incl;
+      const int64_t excl = incl_mine - n_mine;
+      if (pid == 0) prefix_out[tid + 1] = incl_mine;
       locate(X0, tid, excl, n_mine, 0);
       locate(X1, tid, excl, n_mine, 1);
     }
@@ -354,21 +363,18 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     for (int base = 0; base < B; base += kWGThreads) {
       const int b = base + tid;
       const int64_t n = b < B ? ntiles(b) : 0;
-      s_scan[tid] = n;
-      __syncthreads();
-      block_scan();
-      const int64_t incl = running + s_scan[tid], excl = incl - n;
+      int64_t tot;
+      const int64_t incl = running + wg_scan(n, tot), excl = incl - n;
       if (b < B) {
         if (pid == 0) prefix_out[b + 1] = incl;
         locate(X0, b, excl, n, 0);
         locate(X1, b, excl, n, 1);
       }
-      running += s_scan[kWGThreads - 1];
-      __syncthreads();
+      running += tot;
     }
   }
   __syncthreads();
-  const int64_t t_begin = s_t[0], t_end = s_t[1];
+  const int64_t t_begin = s_t[0], t_end = X1 >= C ? W : s_t[1];
   if (t_begin >= t_end) return;                // a range of overhead slots only
 
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;

@@ -87,8 +87,6 @@ constexpr int TE = T * HD;        // elements of one K (or V) tile: 16 KB
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
-typedef float f32x2n __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 // 16-byte global->LDS DMA of one wave: lane i's 16 bytes from `src` land at
@@ -648,16 +646,14 @@ __global__ __launch_bounds__(256) void attn_merge(
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  // piece pq's (m, l) and this thread's 16 values of O / l (read once: non-temporal)
+  // piece pq's (m, l) and this thread's 16 values of O / l (just written by the
+  // main kernel and usually still cached, so ordinary loads)
   auto fetch = [&](int64_t pq, float2 &ml, uint4 &x0, uint4 &x1) {
     const int64_t sq = piece_slot(pq, p_first, Cu, C, Pe);
-    const f32x2n mv = __builtin_nontemporal_load(reinterpret_cast<const f32x2n *>(ws_ml + sq * kRowsPerWG + w * 32 + lq));
     const int64_t f = (sq * (kRowsPerWG * HD / 8)) + ((w * 4 + db) * 64 + lane) * 2;
-    const u32x4n a = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(wo + f));
-    const u32x4n c = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(wo + f + 1));
-    ml = make_float2(mv.x, mv.y);
-    x0 = make_uint4(a.x, a.y, a.z, a.w);
-    x1 = make_uint4(c.x, c.y, c.z, c.w);
+    ml = ws_ml[sq * kRowsPerWG + w * 32 + lq];
+    x0 = wo[f];
+    x1 = wo[f + 1];
   };
   auto absorb = [&](const float2 &ml, const uint4 &x0, const uint4 &x1) {
     if (ml.x > mx) {

@@ -93,7 +93,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // LDS byte address lds_base + 16*i.  Issued through asm so that the compiler
 // does not order later LDS reads behind it (completion is checked with
 // explicit vmcnt waits before the barrier that publishes a tile).  The asm
-// has no outputs.
+// has no outputs.  It loads M0 itself; that is safe only while the compiler
+// keeps nothing of its own in M0, which tests/test_kernel_asm.py checks on
+// the generated assembly.
 __device__ inline void dma16(const void *src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1 nt\n\ts_nop 1"
                :

@@ -428,6 +428,28 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   ld.j = __builtin_amdgcn_readfirstlane(s_loc[2]);
   cur_load(ld, off, total_ctx, max_ctx, S);
   cc = ld;
+  // Q fragments of unit c's rows held by this wave (zeros past M).  A
+  // segment's Q is loaded ahead of use: the first segment's before the first
+  // tiles' DMA, so compute starts once Q and tile 0 have landed; each later
+  // segment's right after the previous segment's last QK, while its last
+  // tile drains.  The compiler waits for these loads before Q's first use;
+  // the tile DMA it does not see only ever makes that wait stricter, as
+  // vector memory operations retire in issue order.
+  bf16x8 qf[8];
+  auto load_q = [&](const Cur &c) {
+    const int g = c.uis / RG, rg = c.uis - (c.uis / RG) * RG;
+    const int row = rg * kRowsPerWG + w * 32 + lq;
+    if (row < M) {
+      const int s = row / G, jh = row - (row / G) * G;
+      const bf16 *p = q + ((int64_t(c.b) * S + s) * Hq + int64_t(g) * G + jh) * HD + lh * 8;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(p + ks * 16);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8{};
+    }
+  };
+  load_q(ld);
   for (int x = 0; x < 2 && t_begin + x < t_end; ++x) {
     issue(ld, x);
     cur_next(ld, UPS, B, off, total_ctx, max_ctx, S);
@@ -439,7 +461,6 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   const int e4 = (lane & 15) >> 2, a4 = lane & 3, gh = (lane >> 4) & 1;
   const int v_lane_off = (lh * 4 + e4) * HD + gh * 16 + a4 * 4;
 
-  bf16x8 qf[8];
   f32x16 o[4];
   f32x16 sA, sB;                 // scores of the two 32-key halves of a tile
   bf16x8 pA[2], pB[2];
@@ -514,21 +535,6 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const int seg_j0 = cc.j;
     const int64_t seg_t1 = min(t_end, t + (cc.n - cc.j));     // one past the segment's last tile
     const Cur cu = cc;                                         // the segment's unit
-    {
-      const int row = rg * kRowsPerWG + w * 32 + lq;
-      if (row < M) {
-        const int s = row / G, jh = row - (row / G) * G;
-        const bf16 *p = q + ((int64_t(cc.b) * S + s) * Hq + int64_t(g) * G + jh) * HD + lh * 8;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(p + ks * 16);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8{};
-      }
-      // Q must have landed before the loop's vmcnt bookkeeping (which counts
-      // only tile DMA) takes over; this drains the tile in flight once per segment.
-      __builtin_amdgcn_s_waitcnt(0xF70);
-    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     m = kNegInf;
@@ -572,6 +578,8 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       steady(true);
       advance();
     }
+    // the next segment's Q (this segment's QK is complete)
+    if (t < t_end) load_q(cc);
     // PV_A and the B half of the segment's last tile (stage st - 1), then the output
     {
       const int stl = (st + NST - 1) & (NST - 1);

@@ -7,8 +7,9 @@
 //
 // bf16, D = 128: attn_bf16_mfma + attn_merge.  A workgroup of 8 waves owns
 // up to 256 query rows (the G heads x S positions that share one KV head,
-// the GQA group), 32 rows per wave, two waves per SIMD so that one wave's
-// softmax overlaps the other's matrix products.  K and V tiles of 64 keys
+// the GQA group), 32 rows per wave, two waves per SIMD; inside each wave the
+// softmax of one 32-key half is interleaved instruction by instruction with
+// the matrix products of the others (step16).  K and V tiles of 64 keys
 // stream from HBM straight into a 4-stage LDS ring (16-byte global->LDS
 // DMA, two tiles in flight while one is consumed), stored row-major with
 // XOR-swizzled 16-byte chunks so every LDS read is bank-conflict free.  Both
@@ -72,8 +73,8 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
 // Work units are (sequence b, KV head g, row group rg); unit u owns the
 // ceil((L_b + S) / 64) key tiles of its sequence, and all units' tiles form
 // one global sequence of W tiles.  Each of the Pe = min(P, W) persistent
-// workgroups scans the ragged lengths itself (in LDS, no separate planning
-// launch) and walks a contiguous range of that sequence, the ranges being
+// workgroups scans the ragged lengths itself (no separate planning launch)
+// and walks a contiguous range of that sequence, the ranges being
 // equal in cost (tiles plus a fixed charge per unit started).  Units a
 // workgroup covers whole are normalised and written directly; where a range
 // cuts a unit, the workgroup writes a partial (O / l in bf16, m, l) into one of its
@@ -82,7 +83,7 @@ __device__ inline void seq_range(const int64_t *off, int b, int64_t total, int m
 // in a second launch keeps the main kernel free of device-scope fences,
 // which on this part write back and invalidate a whole XCD's L2.
 constexpr int T = kKeyTile;       // keys per tile
-constexpr int NST = 4;            // LDS stages: tiles t-1 (its B half), t, and t+1, t+2 landing
+constexpr int NST = 4;            // LDS stages: tile t-1 (its V), tile t, and t+1, t+2 landing
 constexpr int TE = T * HD;        // elements of one K (or V) tile: 16 KB
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -124,8 +125,9 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 // as kSegCost key tiles (the new Q, the pipeline fill and drain, the output),
 // so the split is even in cost, not in tiles: unit (b, g) occupies the cost
 // slots [Cu, Cu + kSegCost + n_b) of a global cost axis, its n_b tiles being
-// the last n_b of them, with Cu = UPS*(prefix_b + kSegCost*b) + g*(n_b + kSegCost)
-// (prefix_b = tiles of the sequences before b, UPS units per sequence).
+// the last n_b of them, with Cu = UPS*(prefix_b + kSegCost*b) + u*(n_b + kSegCost)
+// for the sequence's u-th unit (prefix_b = tiles of the sequences before b,
+// UPS units per sequence).
 // Logical workgroup p owns the slots [X_p, X_{p+1}), X_p = p*C/P, and with them
 // a contiguous (possibly empty) range of the global tile sequence.
 constexpr int kSegCost = 4;

@@ -37,6 +37,14 @@
  *   Layouts    Row-major, innermost index last, no padding.
  *   Results    Deterministic: the same inputs give bitwise-identical outputs
  *              (no floating-point atomics; partials merged in a fixed order).
+ *   Environment  Two variables override the launch plan, for testing the
+ *              work split; results stay correct under either, only the
+ *              speed changes:
+ *                TD_ATTN_GRID=n     persistent attention workgroups (1..4096,
+ *                                   default 256); it also sets the attention
+ *                                   workspace size, so set it before the
+ *                                   workspace query;
+ *                TD_COMMIT_SPLIT=r  vocabulary slices per commit row.
  */
 #ifndef TD_H
 #define TD_H

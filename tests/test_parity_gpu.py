@@ -71,6 +71,41 @@ def test_attn_bf16_shapes(S, Hq, Hkv):
     check_attn(got, oracle_attn(a), f"S={S} Hq={Hq} Hkv={Hkv}")
 
 
+def _random_attn_cases(n=24, seed=4242):
+    """Seeded random valid shapes: ragged lengths with empty and sub-tile
+    contexts and tile-edge lengths, S from 1 to 64, several GQA groupings,
+    and persistent grids from 1 workgroup to more than there are tiles."""
+    rng = np.random.default_rng(seed)
+    heads = [(2, 1), (4, 2), (8, 1), (12, 3), (32, 2), (16, 16), (64, 4), (24, 1)]
+    grids = [None, None, "1", "2", "5", "16", "64", "333"]
+    cases = []
+    for i in range(n):
+        S = int(rng.choice([1, 2, 5, 16, 17, 33, 64]))
+        Hq, Hkv = heads[int(rng.integers(len(heads)))]
+        B = int(rng.integers(1, 9))
+        while B * Hq * S > 4096 and B > 1:
+            B -= 1
+        kinds = rng.integers(0, 4, size=B)
+        lengths = [0 if k == 0 else int(rng.integers(1, 64)) if k == 1 else
+                   int(64 * rng.integers(1, 8) - S) if k == 2 else int(rng.integers(64, 500))
+                   for k in kinds]
+        lengths = [max(0, x) for x in lengths]
+        cases.append((i, B, S, Hq, Hkv, lengths, grids[int(rng.integers(len(grids)))]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_attn_cases(), ids=lambda c: f"r{c[0]}")
+def test_attn_random_shapes(case, monkeypatch):
+    i, B, S, Hq, Hkv, lengths, grid = case
+    if grid:
+        monkeypatch.setenv("TD_ATTN_GRID", grid)
+    w = W["bf16_b8_ctx4k"].with_(B=B, S=S, Hq=Hq, Hkv=Hkv)
+    a = synth.make_attention_inputs(w, 5000 + i, lengths=lengths)
+    log("case attn random", i, "B", B, "S", S, "Hq", Hq, "Hkv", Hkv, "lengths", lengths, "grid", grid)
+    got = run_attn(upload_attn(a), a)
+    check_attn(got, oracle_attn(a), f"random case {i}")
+
+
 def test_attn_unit_variance_and_scale():
     w = W["bf16_b4_ctx64k"].with_(B=2)
     a = synth.make_attention_inputs(w, 23, lengths=[1500, 2100])

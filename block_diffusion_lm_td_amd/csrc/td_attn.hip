@@ -795,14 +795,14 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
     int64_t *prefix = reinterpret_cast<int64_t *>(wsb + p.off_prefix);
     float2 *ws_ml = reinterpret_cast<float2 *>(wsb + p.off_ml);
     bf16 *ws_o = reinterpret_cast<bf16 *>(wsb + p.off_o);
-    hipLaunchKernelGGL(attn_bf16_mfma, dim3(p.grid), dim3(kWGThreads), 0, st,
+    hipLaunchKernelGGL(attn_bf16_mfma, dim3(p.launch), dim3(kWGThreads), 0, st,
                        static_cast<const bf16 *>(a->q), static_cast<const bf16 *>(a->k_blk),
                        static_cast<const bf16 *>(a->v_blk), static_cast<const bf16 *>(a->k_ctx),
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
-                       a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.grid, p.scale_log2,
+                       a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, p.scale_log2,
                        prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out));
     hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
-                       a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.grid, ws_ml, ws_o,
+                       a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
                        static_cast<bf16 *>(a->out));
   } else {
     dim3 grid(p.row_groups, a->Hkv, a->B);

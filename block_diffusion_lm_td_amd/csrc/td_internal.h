@@ -22,7 +22,8 @@ struct AttnPlan {
   int G;                // Hq / Hkv
   int M;                // G * S query rows per (b, kv head)
   int row_groups;       // ceil(M / kRowsPerWG) (MFMA) or ceil(M / 64) (VALU)
-  int grid;             // persistent workgroups (MFMA path)
+  int grid;             // persistent workgroups the workspace holds slots for (MFMA path)
+  int launch;           // workgroups launched (<= grid): fewer when the key tiles are few
   int64_t units;        // B * Hkv * row_groups
   // workspace pieces (byte offsets), MFMA path
   size_t off_prefix;    // int64 [B+1]: tile prefix over sequences (for the merge)

@@ -48,10 +48,23 @@ int validate_commit(const td_commit_args *c, bool check_ptrs) {
   return TD_OK;
 }
 
-static int grid_wgs() {
+static int grid_override() {
   const char *env = getenv("TD_ATTN_GRID");
   if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);
-  return kGridWGs;
+  return 0;
+}
+
+// Workgroups to launch for an estimated W key tiles: one per CU while every
+// workgroup gets at least kMinTilesPerWG tiles, fewer below that, where the
+// per-segment start and the partials would outweigh the extra bandwidth
+// (B = 8 x 4K context: 29.6 us on 160 workgroups against 32.1 us on 256).
+// A multiple of 8 keeps the XCD-aware workgroup mapping.  The choice only
+// affects speed: any grid computes the same result.
+static constexpr int64_t kMinTilesPerWG = 6;
+static int launch_wgs(int64_t tiles_est, int grid) {
+  int64_t n = (tiles_est + kMinTilesPerWG - 1) / kMinTilesPerWG;
+  n = (n + 7) / 8 * 8;
+  return int(std::max<int64_t>(8, std::min<int64_t>(n, grid)));
 }
 
 AttnPlan plan_attn(const td_attn_args *a) {
@@ -63,8 +76,13 @@ AttnPlan plan_attn(const td_attn_args *a) {
   p.scale_log2 = scale * 1.4426950408889634f;
   if (p.mfma) {
     p.row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
-    p.grid = grid_wgs();
     p.units = int64_t(a->B) * a->Hkv * p.row_groups;
+    const int forced = grid_override();
+    p.grid = forced ? forced : kGridWGs;
+    // key tiles: sum over sequences of ceil((L_b + S) / 64), estimated from
+    // the total context (the lengths themselves are on the device)
+    const int64_t seq_tiles = (a->total_ctx + int64_t(a->B) * a->S) / kKeyTile + (a->B + 1) / 2;
+    p.launch = forced ? forced : launch_wgs(int64_t(a->Hkv) * p.row_groups * seq_tiles, p.grid);
     size_t o = 0;
     p.off_prefix = o; o += align256(size_t(a->B + 1) * 8);
     p.off_ml = o;     o += align256(size_t(2) * p.grid * kRowsPerWG * 8);

@@ -303,11 +303,14 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   };
   // inclusive scan of v over the workgroup's threads: shuffles inside each
   // wave, then the wave totals through LDS; also returns the grand total
-  auto wg_scan = [&](int64_t v, int64_t &total) -> int64_t {
+  // (a sequence's tile count is below 2^25 and a sum of 64 of them below
+  // 2^31, as the host bounds max_ctx, so the wave part runs in 32 bits)
+  auto wg_scan = [&](int64_t v64, int64_t &total) -> int64_t {
     const int ln = tid & 63, wv = tid >> 6;
+    uint32_t v = uint32_t(v64);
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int64_t y = __shfl_up(v, d);
+      const uint32_t y = __shfl_up(v, d);
       if (ln >= d) v += y;
     }
     if (ln == 63) s_wsum[wv] = v;
@@ -321,7 +324,13 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       total += x;
     }
     __syncthreads();                           // s_wsum is reused by the next call
-    return v + before;
+    return int64_t(v) + before;
+  };
+  // a workgroup-uniform 64-bit value held in vector registers, moved to scalar ones
+  auto uniform64 = [](int64_t x) -> int64_t {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
   };
   const bool one_pass = B <= kWGThreads;
   int64_t n_mine = 0, incl_mine = 0, wseq = 0;
@@ -335,6 +344,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
       wseq += tot;
     }
   }
+  wseq = uniform64(wseq);
   const int64_t W = wseq * UPS;
   const int Pe = int(W < P ? W : P);          // logical workgroups with work
   if (pid >= Pe) return;
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     }
   }
   __syncthreads();
-  const int64_t t_begin = s_t[0], t_end = X1 >= C ? W : s_t[1];
+  const int64_t t_begin = uniform64(s_t[0]), t_end = uniform64(X1 >= C ? W : s_t[1]);
   if (t_begin >= t_end) return;                // a range of overhead slots only
 
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;

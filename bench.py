@@ -146,6 +146,7 @@ def block_loop(args, L):
     def up(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    CHUNK = 8
     for S in (16, 32, 64):
         w0 = synth.WORKLOADS["bf16_b32_ctx2k_loop"].with_(S=S)
         a = synth.make_attention_inputs(w0, args.seed + S)
@@ -183,6 +184,8 @@ def block_loop(args, L):
                 done_at = np.zeros(B, np.int64)
                 ms = 0.0
                 steps = 0
+                torch.cuda.synchronize()
+                t_wall = time.perf_counter()
                 while True:
                     logits.view(-1, w.V)[rows, peak_d] = stored_d[steps]
                     e0 = torch.cuda.Event(enable_timing=True)
@@ -202,10 +205,55 @@ def block_loop(args, L):
                     if steps >= S:
                         raise RuntimeError("a block did not finish within S steps")
                     o["masked_in"].copy_(o["masked_out"])
-                return steps, done_at, ms
+                return steps, done_at, ms, (time.perf_counter() - t_wall) * 1e3
+
+            # the same loop resident on the device: steps of td_denoise_step_if, each
+            # gated by the previous step's n_masked_left (two counters used
+            # alternately), masks updated in place.  Steps go out in chunks of
+            # CHUNK with one synchronisation per chunk: a gated-off step still
+            # costs the dispatch of its kernels, so enqueueing all S at once would
+            # pay for up to S - 1 of them.
+            cnt = torch.zeros((2,), dtype=torch.int32, device=dev)
+            cd = [td.commit_args(logits, o["commit"], o["token"], gamma, o["masked_in"],
+                                 o["maxprob"], o["n_commit"], o["masked_in"], o["tokens"],
+                                 cnt[k:k + 1]) for k in range(2)]
+            gates = [ctypes.c_void_p(cnt[k:k + 1].data_ptr()) for k in range(2)]
+
+            def run_block_device():
+                o["masked_in"].fill_(1)
+                o["tokens"].fill_(-1)
+                cnt.fill_(0)
+                cnt[1] = 1
+                torch.cuda.synchronize()
+                t_wall = time.perf_counter()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                k = 0
+                while k < S:
+                    for _ in range(min(CHUNK, S - k)):
+                        logits.view(-1, w.V)[rows, peak_d] = stored_d[k]
+                        r = L.td_denoise_step_if(ctypes.byref(aa), ctypes.byref(cd[k % 2]),
+                                                 gates[(k + 1) % 2], wsp, ws.numel(), sp)
+                        if r != 0:
+                            raise RuntimeError(_td.status_str(r))
+                        k += 1
+                    if int(cnt[(k + 1) % 2].item()) == 0:     # the last step's n_masked_left
+                        break
+                e1.record(stream)
+                torch.cuda.synchronize()
+                wall = (time.perf_counter() - t_wall) * 1e3
+                if int(o["masked_in"].sum().item()) != 0:
+                    raise RuntimeError("the device-resident loop left positions masked")
+                return e0.elapsed_time(e1), wall
 
             run_block(False)                       # warm-up pass
-            steps, done_at, ms = run_block(True)
+            steps, done_at, ms, wall_host = run_block(True)
+            tokens_host = o["tokens"].clone()
+            run_block_device()                     # warm-up pass
+            dev_ms, dev_wall = run_block_device()
+            if not torch.equal(o["tokens"], tokens_host):
+                raise RuntimeError("device-resident loop committed different tokens")
             committed = B * S
             print(json.dumps({
                 "metric": "block loop: steps per block and committed tokens/s",
@@ -214,7 +262,12 @@ def block_loop(args, L):
                 "loop_steps": steps, "steps_per_block_mean": round(float(done_at.mean()), 3),
                 "steps_per_block_max": int(done_at.max()),
                 "ms_total": round(ms, 4), "ms_per_step": round(ms / steps, 5),
-                "committed_tokens_per_s": round(committed / (ms * 1e-3), 1)}), flush=True)
+                "committed_tokens_per_s": round(committed / (ms * 1e-3), 1),
+                "host_driven_wall_ms": round(wall_host, 4),
+                "device_resident": {"chunk": CHUNK, "gpu_ms": round(dev_ms, 4),
+                                    "wall_ms": round(dev_wall, 4),
+                                    "committed_tokens_per_s": round(committed / (dev_wall * 1e-3), 1)}}),
+                  flush=True)
             del logits, stored_d, ws
 
 

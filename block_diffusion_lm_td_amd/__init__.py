@@ -15,4 +15,5 @@ from ._td import (  # noqa: F401
     td_block_attn,
     td_commit,
     td_denoise_step,
+    td_denoise_step_if,
 )

@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "td_block_attn": (c_int, [A, c_void_p, c_size_t, c_void_p]),
             "td_commit": (c_int, [C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step": (c_int, [A, C, c_void_p, c_size_t, c_void_p]),
+            "td_denoise_step_if": (c_int, [A, C, c_void_p, c_void_p, c_size_t, c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -222,3 +223,17 @@ def td_denoise_step(attn: TdAttnArgs, commit: TdCommitArgs, *, workspace=None, d
     ptr, n = _ws(workspace, device).get(need)
     check(L.td_denoise_step(ctypes.byref(attn), ctypes.byref(commit), ptr, n, _stream(stream)),
           "td_denoise_step")
+
+
+def td_denoise_step_if(attn: TdAttnArgs, commit: TdCommitArgs, gate, *, workspace=None,
+                       device=None, stream=None):
+    """td_denoise_step gated by the device int32 tensor ``gate`` (shape (1,)):
+    the step runs when it holds a nonzero value when the step starts on the
+    device, and otherwise only clears the commit's n_masked_left."""
+    torch = _torch()
+    L = lib()
+    g = _ptr(gate, "gate", torch.int32, (1,))
+    need = L.td_denoise_workspace_bytes(ctypes.byref(attn), ctypes.byref(commit))
+    ptr, n = _ws(workspace, device).get(need)
+    check(L.td_denoise_step_if(ctypes.byref(attn), ctypes.byref(commit), c_void_p(g), ptr, n,
+                               _stream(stream)), "td_denoise_step_if")

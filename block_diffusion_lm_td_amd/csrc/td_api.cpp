@@ -15,6 +15,23 @@ int check_ws(size_t need, void *ws, size_t ws_bytes) {
   return TD_OK;
 }
 
+int denoise(const td_attn_args *a, const td_commit_args *c, const int32_t *gate, void *ws,
+            size_t ws_bytes, td_stream_t stream) {
+  int rc = validate_attn(a, true);
+  if (rc != TD_OK) return rc;
+  rc = validate_commit(c, true);
+  if (rc != TD_OK) return rc;
+  if (a->B != c->B || a->S != c->S) return TD_ERR_INVALID;
+  const AttnPlan pa = plan_attn(a);
+  const CommitPlan pc = plan_commit(c);
+  const size_t wa = align256(pa.ws_bytes), wc = align256(pc.ws_bytes);
+  rc = check_ws(wa + wc, ws, ws_bytes);
+  if (rc != TD_OK) return rc;
+  rc = launch_attn(a, pa, ws, stream, gate);
+  if (rc != TD_OK) return rc;
+  return launch_commit(c, pc, static_cast<char *>(ws) + wa, stream, gate);
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,19 +86,13 @@ int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t st
 
 int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws, size_t ws_bytes,
                     td_stream_t stream) {
-  int rc = validate_attn(a, true);
-  if (rc != TD_OK) return rc;
-  rc = validate_commit(c, true);
-  if (rc != TD_OK) return rc;
-  if (a->B != c->B || a->S != c->S) return TD_ERR_INVALID;
-  const AttnPlan pa = plan_attn(a);
-  const CommitPlan pc = plan_commit(c);
-  const size_t wa = align256(pa.ws_bytes), wc = align256(pc.ws_bytes);
-  rc = check_ws(wa + wc, ws, ws_bytes);
-  if (rc != TD_OK) return rc;
-  rc = launch_attn(a, pa, ws, stream);
-  if (rc != TD_OK) return rc;
-  return launch_commit(c, pc, static_cast<char *>(ws) + wa, stream);
+  return denoise(a, c, nullptr, ws, ws_bytes, stream);
+}
+
+int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
+                       void *ws, size_t ws_bytes, td_stream_t stream) {
+  if (!gate || !c || gate == c->n_masked_left) return TD_ERR_INVALID;
+  return denoise(a, c, gate, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -280,7 +280,8 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const bf16 *__restrict__ kc, const bf16 *__restrict__ vc, const int64_t *__restrict__ off,
     int64_t total_ctx, int max_ctx, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     float sl2, int64_t *__restrict__ prefix_out, float2 *__restrict__ ws_ml,
-    bf16 *__restrict__ ws_o, bf16 *__restrict__ out) {
+    bf16 *__restrict__ ws_o, bf16 *__restrict__ out, const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;           // a gated step whose block has finished
   // K and V tiles, row-major [key][d] with 16-byte chunks XOR-swizzled per row:
   // K chunk c of key r sits at c ^ (r % 16), V chunk c at c ^ 4*(r % 4).
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NST * TE];
@@ -645,7 +646,9 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
 // order with a running max (one pass, deterministic).
 __global__ __launch_bounds__(256) void attn_merge(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
-    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out) {
+    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
+    const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
   const int UPS = Hkv * RG;
   const int64_t u = blockIdx.x >> 3;
   const int w = blockIdx.x & 7;
@@ -738,7 +741,8 @@ __global__ __launch_bounds__(64) void attn_valu(
     const T *__restrict__ q, const T *__restrict__ kb, const T *__restrict__ vb,
     const T *__restrict__ kc, const T *__restrict__ vc, const int64_t *__restrict__ off,
     int64_t total_ctx, int max_ctx, int S, int Hq, int Hkv, int G, int M, float sl2,
-    T *__restrict__ out) {
+    T *__restrict__ out, const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
   __shared__ float Kt[32][DD];
   __shared__ float Vt2[32][DD];
   const int g = blockIdx.y, b = blockIdx.z;
@@ -797,7 +801,8 @@ __global__ __launch_bounds__(64) void attn_valu(
 
 }  // namespace
 
-int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream) {
+int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
+                const int32_t *gate) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int max_ctx = int(a->max_ctx);
   if (p.mfma) {
@@ -810,10 +815,10 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                        static_cast<const bf16 *>(a->v_blk), static_cast<const bf16 *>(a->k_ctx),
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
                        a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, p.scale_log2,
-                       prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out));
+                       prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out), gate);
     hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
                        a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
-                       static_cast<bf16 *>(a->out));
+                       static_cast<bf16 *>(a->out), gate);
   } else {
     dim3 grid(p.row_groups, a->Hkv, a->B);
 #define TD_VALU(T, DD)                                                                         \
@@ -821,7 +826,7 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                      static_cast<const T *>(a->q), static_cast<const T *>(a->k_blk),         \
                      static_cast<const T *>(a->v_blk), static_cast<const T *>(a->k_ctx),     \
                      static_cast<const T *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx, \
-                     a->S, a->Hq, a->Hkv, p.G, p.M, p.scale_log2, static_cast<T *>(a->out))
+                     a->S, a->Hq, a->Hkv, p.G, p.M, p.scale_log2, static_cast<T *>(a->out), gate)
     if (a->dtype == TD_F32) {
       if (a->D == 64) TD_VALU(float, 64); else TD_VALU(float, 128);
     } else {

@@ -87,13 +87,16 @@ __device__ inline void absorb(const float (&f)[NV], int vi, float &m, float &z, 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void commit_rows(const T *__restrict__ logits, int V, int span,
                                                    int R, Part *__restrict__ parts,
-                                                   int32_t *__restrict__ n_masked_left) {
+                                                   int32_t *__restrict__ n_masked_left,
+                                                   const int32_t *__restrict__ gate) {
   typedef typename Vec<T>::type VT;
   constexpr int NV = Vec<T>::n;
   const int64_t row = blockIdx.x / R;
   const int r = blockIdx.x - int(row) * R;
   const int tid = threadIdx.x;
+  // cleared even in a gated-off step, so that a chain of gated steps stays off
   if (blockIdx.x == 0 && tid == 0 && n_masked_left) *n_masked_left = 0;
+  if (gate && *gate == 0) return;
   const int e_lo = r * span;
   const int e_hi = min(V, e_lo + span);
   const T *x = logits + row * V;
@@ -180,7 +183,8 @@ __global__ __launch_bounds__(64) void commit_finalize(
     const Part *__restrict__ parts, int S, int R, float gamma, const uint8_t *masked_in,
     uint8_t *__restrict__ commit, int32_t *__restrict__ token, float *__restrict__ maxprob,
     int32_t *__restrict__ n_commit, uint8_t *masked_out, int32_t *__restrict__ tokens,
-    int32_t *__restrict__ n_masked_left) {
+    int32_t *__restrict__ n_masked_left, const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const bool act = i < S;
@@ -234,28 +238,29 @@ __global__ __launch_bounds__(64) void commit_finalize(
 
 }  // namespace
 
-int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream) {
+int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
+                  const int32_t *gate) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Part *parts = reinterpret_cast<Part *>(ws);
   const unsigned nblk = unsigned(p.rows * p.R);
   if (c->dtype == TD_BF16) {
     if (p.vec)
       hipLaunchKernelGGL((commit_rows<bf16, true>), dim3(nblk), dim3(256), 0, st,
-                         static_cast<const bf16 *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left);
+                         static_cast<const bf16 *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
     else
       hipLaunchKernelGGL((commit_rows<bf16, false>), dim3(nblk), dim3(256), 0, st,
-                         static_cast<const bf16 *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left);
+                         static_cast<const bf16 *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
   } else {
     if (p.vec)
       hipLaunchKernelGGL((commit_rows<float, true>), dim3(nblk), dim3(256), 0, st,
-                         static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left);
+                         static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
     else
       hipLaunchKernelGGL((commit_rows<float, false>), dim3(nblk), dim3(256), 0, st,
-                         static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left);
+                         static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
   }
   hipLaunchKernelGGL(commit_finalize, dim3(c->B), dim3(64), 0, st, parts, c->S, p.R, c->gamma,
                      c->masked_in, c->commit, c->token, c->maxprob, c->n_commit, c->masked_out,
-                     c->tokens, c->n_masked_left);
+                     c->tokens, c->n_masked_left, gate);
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }
 

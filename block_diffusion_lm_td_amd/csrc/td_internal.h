@@ -50,7 +50,11 @@ CommitPlan plan_commit(const td_commit_args *c);
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Launchers (td_attn.hip / td_commit.hip); return a td_status.
-int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream);
-int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream);
+// gate: NULL, or a device int32 that every kernel reads first; 0 = do nothing
+// (the commit still clears n_masked_left)
+int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
+                const int32_t *gate = nullptr);
+int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
+                  const int32_t *gate = nullptr);
 
 }  // namespace td

@@ -158,6 +158,24 @@ int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t st
 int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws,
                     size_t ws_bytes, td_stream_t stream);
 
+/* td_denoise_step gated by a device value, so that a block's whole step loop
+ * (chathome, block-generation paragraph: a block is refined step by step
+ * until every position has committed) can be enqueued with no host
+ * synchronisation.  `gate` is a DEVICE int32 that every kernel of the step
+ * reads first:
+ *   *gate != 0  the step runs exactly as td_denoise_step;
+ *   *gate == 0  the step does nothing, except that c->n_masked_left (if not
+ *               NULL) is set to 0; no other output is written.
+ * Passing the previous step's n_masked_left as the gate runs the steps while
+ * positions remain masked and turns the rest into no-ops; since each step
+ * commits at least one position per unfinished block, S such steps always
+ * suffice.  The gate must not be this step's own c->n_masked_left (two
+ * counters used alternately are the usual pattern).
+ * Returns TD_ERR_INVALID for a NULL gate or one equal to c->n_masked_left;
+ * otherwise as td_denoise_step. */
+int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
+                       void *ws, size_t ws_bytes, td_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,6 +123,21 @@ def test_denoise_step_checks(L):
     assert L.td_denoise_step(ctypes.byref(a_bad), ctypes.byref(c), ctypes.c_void_p(FAKE), need, None) == UNSUPPORTED
 
 
+def test_denoise_step_if_gate_checks(L):
+    """The gate must be given and must not be the step's own n_masked_left
+    (which the commit clears); otherwise the checks are td_denoise_step's."""
+    a = attn()
+    c = commit(n_masked_left=FAKE + 4096)
+    need = L.td_denoise_workspace_bytes(ctypes.byref(a), ctypes.byref(c))
+    ws = ctypes.c_void_p(FAKE)
+    step_if = L.td_denoise_step_if
+    assert step_if(ctypes.byref(a), ctypes.byref(c), None, ws, need, None) == INVALID
+    assert step_if(ctypes.byref(a), ctypes.byref(c), ctypes.c_void_p(FAKE + 4096), ws, need, None) == INVALID
+    assert step_if(ctypes.byref(a), ctypes.byref(c), ctypes.c_void_p(FAKE + 8192), None, need, None) == WORKSPACE
+    c2 = commit(S=8)
+    assert step_if(ctypes.byref(a), ctypes.byref(c2), ctypes.c_void_p(FAKE + 8192), ws, need, None) == INVALID
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 16, 4, 64)

@@ -341,3 +341,118 @@ def test_block_loop_teacher_forced(S, gamma):
         steps += 1
     assert (tokens >= 0).all()
     log(f"[loop] S={S} gamma={gamma}: steps={steps}")
+
+
+# ----------------------------------------------------------------------------
+# gated step: a block's whole loop enqueued with no host synchronisation
+# ----------------------------------------------------------------------------
+def _loop_setup(S, gamma, seed):
+    w = W["bf16_b32_ctx2k_loop"].with_(B=8, S=S, V=16384, gamma=gamma)
+    a = synth.make_attention_inputs(w, seed, lengths=[300, 0, 700, 64, 129, 1000, 5, 450])
+    base, peak, stored = synth.loop_peak_values(w, seed + 1, S + 1)
+    d = upload_attn(a)
+    logits = dev(base, "bf16").view(w.B, w.S, w.V)
+    return w, a, d, logits, torch.from_numpy(peak).to("cuda"), dev(stored, "bf16")
+
+
+def _commit_bufs(B, S):
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device="cuda")
+    return dict(commit=z((B, S), torch.uint8), token=z((B, S), torch.int32),
+                maxprob=z((B, S), torch.float32), n_commit=z((B,), torch.int32),
+                masked=torch.ones((B, S), dtype=torch.uint8, device="cuda"),
+                tokens=torch.full((B, S), -1, dtype=torch.int32, device="cuda"))
+
+
+def _cargs(logits, c, gamma, n_left):
+    return td.commit_args(logits, c["commit"], c["token"], gamma, c["masked"], c["maxprob"],
+                          c["n_commit"], c["masked"], c["tokens"], n_left)
+
+
+def test_denoise_step_if_gate_zero_and_one():
+    """gate = 0: nothing is written except n_masked_left = 0; gate = 1: the
+    same outputs as td_denoise_step."""
+    w, a, d, logits, peak, stored = _loop_setup(16, 0.8, 6100)
+    B, S = w.B, w.S
+    L = td.lib()
+    out = torch.full_like(d["q"], 3.0)
+    aa = td.attn_args(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["offsets"], out,
+                      a["total_ctx"], a["max_ctx"])
+    c = _commit_bufs(B, S)
+    for k in ("commit", "token", "n_commit"):
+        c[k].fill_(7)
+    c["maxprob"].fill_(-1.0)
+    n_left = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    cc = _cargs(logits, c, w.gamma, n_left)
+    gate = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    log("case gated step, gate 0")
+    td.td_denoise_step_if(aa, cc, gate)
+    torch.cuda.synchronize()
+    assert int(n_left.item()) == 0
+    assert bool((out == 3.0).all()), "attention wrote with gate 0"
+    assert bool((c["commit"] == 7).all()) and bool((c["token"] == 7).all())
+    assert bool((c["n_commit"] == 7).all()) and bool((c["maxprob"] == -1.0).all())
+    assert bool((c["masked"] == 1).all()) and bool((c["tokens"] == -1).all())
+
+    log("case gated step, gate 1 vs td_denoise_step")
+    gate.fill_(1)
+    td.td_denoise_step_if(aa, cc, gate)
+    ref = _commit_bufs(B, S)
+    out_ref = torch.empty_like(d["q"])
+    n_ref = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    aa_ref = td.attn_args(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["offsets"],
+                          out_ref, a["total_ctx"], a["max_ctx"])
+    td.td_denoise_step(aa_ref, _cargs(logits, ref, w.gamma, n_ref))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    for k in ("commit", "token", "maxprob", "n_commit", "masked", "tokens"):
+        assert torch.equal(c[k], ref[k]), k
+    assert int(n_left.item()) == int(n_ref.item())
+
+
+@pytest.mark.parametrize("S", [16, 64])
+def test_block_loop_device_resident(S):
+    """S gated steps enqueued back to back, the gate of each step being the
+    previous step's n_masked_left (two counters used alternately), with one
+    synchronisation at the end, give exactly the host-driven loop's result
+    (which test_block_loop_teacher_forced checks against the oracle)."""
+    gamma = 0.8
+    w, a, d, logits, peak, stored = _loop_setup(S, gamma, 6200 + S)
+    B = w.B
+    rows = torch.arange(B * S, device="cuda")
+    aa = td.attn_args(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["offsets"],
+                      torch.empty_like(d["q"]), a["total_ctx"], a["max_ctx"])
+
+    # host-driven: a synchronisation after every step
+    log("case device-resident loop S", S, "host-driven reference")
+    h = _commit_bufs(B, S)
+    n_h = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ch = _cargs(logits, h, gamma, n_h)
+    left_h = []
+    while True:
+        logits.view(-1, w.V)[rows, peak] = stored[len(left_h)]
+        td.td_denoise_step(aa, ch)
+        left_h.append(int(n_h.item()))
+        if left_h[-1] == 0:
+            break
+        assert len(left_h) < S, "block did not finish within S steps"
+    tokens_h, masked_h = h["tokens"].clone(), h["masked"].clone()
+
+    # device-resident: S gated steps, no synchronisation until the end
+    log("case device-resident loop S", S, "gated")
+    g = _commit_bufs(B, S)
+    cnt = torch.zeros((2,), dtype=torch.int32, device="cuda")
+    cnt[1] = 1                                        # opens step 0
+    cg = [_cargs(logits, g, gamma, cnt[k:k + 1]) for k in range(2)]
+    hist = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+    for k in range(S):
+        logits.view(-1, w.V)[rows, peak] = stored[k]
+        td.td_denoise_step_if(aa, cg[k % 2], cnt[(k + 1) % 2:(k + 1) % 2 + 1])
+        hist[k:k + 1].copy_(cnt[k % 2:k % 2 + 1])
+    torch.cuda.synchronize()
+    hist = hist.cpu().numpy().tolist()
+    n = len(left_h)
+    assert hist[:n] == left_h, (hist, left_h)
+    assert all(x == 0 for x in hist[n:]), hist
+    assert torch.equal(g["tokens"], tokens_h) and torch.equal(g["masked"], masked_h)
+    assert bool((g["tokens"] >= 0).all())
+    log(f"[device loop] S={S}: {n} steps of {S} enqueued")

@@ -9,4 +9,5 @@ from .td_oracle import (  # noqa: F401
     confidence_commit,
     denoise_step,
     denoise_loop,
+    cache_append,
 )

@@ -168,3 +168,31 @@ def denoise_loop(step_logits, B, S, gamma, max_steps=None):
         t += 1
     return dict(steps=t, tokens=tokens, commits_per_step=np.array(per_step),
                 steps_per_seq=steps_per_seq, done=not masked.any())
+
+
+# ----------------------------------------------------------------------------
+# Context-cache append after a block has committed
+# ([chathome] block-generation paragraph)
+# ----------------------------------------------------------------------------
+def cache_append(k_ctx, v_ctx, offsets, k_new, v_new):
+    """Context-cache update after a block has committed: every sequence's
+    cached keys/values are followed by the block's S rows, in a new packed
+    cache ([chathome] block-generation paragraph: once a block is done, the
+    context tower takes in the committed tokens and its per-layer KV cache
+    grows by them).
+
+    k_ctx, v_ctx [T, Hkv, D] packed by ``offsets`` [B+1]; k_new, v_new
+    [B, S, Hkv, D].  Returns (k_out, v_out, offsets_out) with sequence b at
+    rows offsets_out[b] .. offsets_out[b+1] of k_out / v_out: its L_b old rows,
+    then its S new ones."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    B, S = k_new.shape[0], k_new.shape[1]
+    ks, vs = [], []
+    offsets_out = np.zeros(B + 1, dtype=np.int64)
+    for b in range(B):
+        start, stop = int(offsets[b]), int(offsets[b + 1])
+        ks.append(np.concatenate([k_ctx[start:stop], k_new[b]], axis=0))
+        vs.append(np.concatenate([v_ctx[start:stop], v_new[b]], axis=0))
+        offsets_out[b + 1] = offsets_out[b] + (stop - start) + S
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0), offsets_out
+

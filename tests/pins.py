@@ -443,3 +443,125 @@ def pin_step_masks(step):
 
 LOOP_PINS = [pin_loop_force_one_is_ar, pin_loop_low_gamma_one_step, pin_loop_steps_monotone]
 STEP_PINS = [pin_step_masks]
+
+
+# ----------------------------------------------------------------------------
+# cache-append pins ([chathome] block-generation paragraph)
+# ----------------------------------------------------------------------------
+def _labelled_cache(lengths, S, Hkv=2, D=3):
+    """Rows whose values name (sequence, time index, tensor): old row t of
+    sequence b is (b, t), new row s is (b, L_b + s); K and V differ in sign."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = len(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(off[-1])
+    k_ctx = np.zeros((T, Hkv, D))
+    k_new = np.zeros((B, S, Hkv, D))
+    for b in range(B):
+        for t in range(int(lengths[b])):
+            k_ctx[off[b] + t] = 1000.0 * (b + 1) + t
+        for s in range(S):
+            k_new[b, s] = 1000.0 * (b + 1) + lengths[b] + s
+    k_ctx[..., 1:] += 0.5                  # the head / lane index stays visible
+    k_new[..., 1:] += 0.5
+    return k_ctx, -k_ctx, off, k_new, -k_new
+
+
+def pin_append_time_order(append):
+    """Reading the new cache row by row gives every sequence's keys in time
+    order, sequence after sequence: a stable sort of all rows by (sequence,
+    time) -- a different route to the same layout."""
+    lengths, S = [3, 0, 5, 1], 2
+    k_ctx, v_ctx, off, k_new, v_new = _labelled_cache(lengths, S)
+    k_out, v_out, off_out = append(k_ctx, v_ctx, off, k_new, v_new)
+    rows = np.concatenate([k_ctx, k_new.reshape(-1, *k_ctx.shape[1:])], axis=0)
+    key = rows[:, 0, 0]
+    want = rows[np.lexsort((key % 1000.0, key // 1000.0))]
+    assert np.array_equal(np.asarray(k_out), want)
+    assert np.array_equal(np.asarray(v_out), -want)
+    assert np.array_equal(np.asarray(off_out), np.searchsorted(want[:, 0, 0] // 1000.0,
+                                                               np.arange(1, len(lengths) + 2)))
+
+
+def pin_append_offsets_closed_form(append):
+    """Sequence b moves down by b*S rows and grows by S."""
+    rng = np.random.default_rng(45)
+    lengths, S = np.array([0, 7, 2, 0, 11]), 3
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    T, B = int(off[-1]), len(lengths)
+    k_ctx = rng.standard_normal((T, 2, 4))
+    k_new = rng.standard_normal((B, S, 2, 4))
+    _, _, off_out = append(k_ctx, k_ctx, off, k_new, k_new)
+    off_out = np.asarray(off_out)
+    assert np.array_equal(off_out, off + S * np.arange(B + 1))
+    assert np.array_equal(np.diff(off_out), lengths + S)
+
+
+def pin_append_identities(append):
+    """S = 0 leaves the cache as it was; an empty cache becomes the new rows."""
+    rng = np.random.default_rng(46)
+    lengths = [4, 0, 2]
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    k_ctx = rng.standard_normal((6, 1, 5))
+    v_ctx = rng.standard_normal((6, 1, 5))
+    k_out, v_out, off_out = append(k_ctx, v_ctx, off, np.zeros((3, 0, 1, 5)),
+                                   np.zeros((3, 0, 1, 5)))
+    assert np.array_equal(np.asarray(k_out), k_ctx) and np.array_equal(np.asarray(v_out), v_ctx)
+    assert np.array_equal(np.asarray(off_out), off)
+    k_new = rng.standard_normal((3, 4, 1, 5))
+    v_new = rng.standard_normal((3, 4, 1, 5))
+    k_out, v_out, off_out = append(np.zeros((0, 1, 5)), np.zeros((0, 1, 5)),
+                                   np.zeros(4, np.int64), k_new, v_new)
+    assert np.array_equal(np.asarray(k_out), k_new.reshape(12, 1, 5))
+    assert np.array_equal(np.asarray(v_out), v_new.reshape(12, 1, 5))
+    assert np.array_equal(np.asarray(off_out), [0, 4, 8, 12])
+
+
+def pin_append_two_blocks_at_once(append):
+    """Appending S1 rows and then S2 rows equals appending the S1 + S2 rows
+    in one call."""
+    rng = np.random.default_rng(47)
+    lengths = [2, 5, 0]
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    k_ctx, v_ctx = rng.standard_normal((7, 2, 3)), rng.standard_normal((7, 2, 3))
+    k1, v1 = rng.standard_normal((3, 2, 2, 3)), rng.standard_normal((3, 2, 2, 3))
+    k2, v2 = rng.standard_normal((3, 3, 2, 3)), rng.standard_normal((3, 3, 2, 3))
+    ka, va, oa = append(k_ctx, v_ctx, off, k1, v1)
+    ka, va, oa = append(ka, va, oa, k2, v2)
+    kb, vb, ob = append(k_ctx, v_ctx, off, np.concatenate([k1, k2], axis=1),
+                        np.concatenate([v1, v2], axis=1))
+    assert np.array_equal(np.asarray(ka), np.asarray(kb))
+    assert np.array_equal(np.asarray(va), np.asarray(vb))
+    assert np.array_equal(np.asarray(oa), np.asarray(ob))
+
+
+def pin_append_then_attend(append):
+    """Attention over the grown cache (torch SDPA, keys read from the new
+    rows of sequence b) equals attention over the keys [old cache ; block]
+    with the block's rows moved into the cache -- the next block then sees
+    the committed tokens as context."""
+    rng = np.random.default_rng(48)
+    B, S, Hq, Hkv, D = 3, 4, 4, 2, 8
+    a = rand_attn(rng, B, S, Hq, Hkv, D, [5, 0, 3])
+    k_out, v_out, off_out = append(a["k_ctx"], a["v_ctx"], a["offsets"], a["k_blk"], a["v_blk"])
+    q_next = rng.standard_normal((B, S, Hq, D))
+    kb_next = rng.standard_normal((B, S, Hkv, D))
+    vb_next = rng.standard_normal((B, S, Hkv, D))
+    grown = dict(q=q_next, k_blk=kb_next, v_blk=vb_next, k_ctx=np.asarray(k_out),
+                 v_ctx=np.asarray(v_out), offsets=np.asarray(off_out))
+    for b in range(B):
+        want_keys = np.concatenate([a["k_ctx"][a["offsets"][b]:a["offsets"][b + 1]],
+                                    a["k_blk"][b], kb_next[b]], axis=0)
+        want_vals = np.concatenate([a["v_ctx"][a["offsets"][b]:a["offsets"][b + 1]],
+                                    a["v_blk"][b], vb_next[b]], axis=0)
+        tq = torch.from_numpy(np.ascontiguousarray(q_next[b].transpose(1, 0, 2)))[None]
+        tk = torch.from_numpy(np.ascontiguousarray(want_keys.transpose(1, 0, 2)))[None]
+        tv = torch.from_numpy(np.ascontiguousarray(want_vals.transpose(1, 0, 2)))[None]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        _close(sdpa_seq(grown, b), want, what=f"sequence {b}")
+
+
+APPEND_PINS = [pin_append_time_order, pin_append_offsets_closed_form, pin_append_identities,
+               pin_append_two_blocks_at_once, pin_append_then_attend]
+

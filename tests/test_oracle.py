@@ -28,3 +28,8 @@ def test_loop_pin(pin):
 @pytest.mark.parametrize("pin", pins.STEP_PINS, ids=lambda f: f.__name__)
 def test_step_pin(pin):
     pin(oracle.denoise_step)
+
+
+@pytest.mark.parametrize("pin", pins.APPEND_PINS, ids=lambda f: f.__name__)
+def test_append_pin(pin):
+    pin(oracle.cache_append)

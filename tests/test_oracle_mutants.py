@@ -39,6 +39,15 @@ MUTANTS = [
     ("step_writes_all_tokens", "tokens[c[\"commit\"]] = c[\"token\"][c[\"commit\"]]\n    return dict(out=out",
      "tokens[:] = c[\"token\"]\n    return dict(out=out"),
     ("loop_remasks", "masked &= ~c[\"commit\"]", "masked = ~c[\"commit\"]"),
+    ("append_new_rows_first", "np.concatenate([k_ctx[start:stop], k_new[b]], axis=0)",
+     "np.concatenate([k_new[b], k_ctx[start:stop]], axis=0)"),
+    ("append_values_from_keys", "np.concatenate([v_ctx[start:stop], v_new[b]], axis=0)",
+     "np.concatenate([v_ctx[start:stop], k_new[b]], axis=0)"),
+    ("append_offsets_without_block", "offsets_out[b] + (stop - start) + S",
+     "offsets_out[b] + (stop - start)"),
+    ("append_drops_last_old_row", "k_ctx[start:stop], k_new[b]", "k_ctx[start:stop - 1], k_new[b]"),
+    ("append_neighbours_rows", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b - 1]]"),
+    ("append_new_rows_truncated", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b, 1:]]"),
 ]
 
 
@@ -57,6 +66,7 @@ def _all_pins(mod):
     yield from ((p, mod.confidence_commit) for p in pins.COMMIT_PINS)
     yield from ((p, mod.denoise_loop) for p in pins.LOOP_PINS)
     yield from ((p, mod.denoise_step) for p in pins.STEP_PINS)
+    yield from ((p, mod.cache_append) for p in pins.APPEND_PINS)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

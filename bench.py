@@ -28,6 +28,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 ATTN_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_bf16_b64_ragged1k_8k.json")
+APPEND_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_append.hip")
+APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_traffic_bf16_b64_ragged1k_8k.json")
 
 
 def log(*a):
@@ -59,18 +61,28 @@ def source_sha(path):
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the attention kernels from committed rocprofv3
-    counter runs on this workload, valid only while the kernel source is
-    unchanged."""
+def measured_traffic(workload, src=None, path=None):
+    """HBM bytes per launch of a kernel (default: the attention kernels) from
+    committed rocprofv3 counter runs on this workload, valid only while the
+    kernel source is unchanged."""
+    src = ATTN_SRC if src is None else src
+    path = TRAFFIC_FILE if path is None else path
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(ATTN_SRC) or t.get("workload") != workload:
+    if t.get("source_sha") != source_sha(src) or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
+
+
+def append_algorithmic(w, total_ctx):
+    """Bytes one context-cache append must move: every old and new row of K
+    and V read once and written once, plus the offsets read and written."""
+    e = 2 if w.dtype == "bf16" else 4
+    rows = total_ctx + w.B * w.S
+    return 4 * rows * w.Hkv * w.D * e + 16 * (w.B + 1)
 
 
 def cpu_baseline(w, a, c, el, budget_s):
@@ -271,6 +283,116 @@ def block_loop(args, L):
             del logits, stored_d, ws
 
 
+def cache_append_bench(args, L):
+    """td_cache_append on the batched workload's cache: the 64 sequences'
+    1K..8K cached rows (2 KV heads x 128 bf16, K and V) grow by the block's 16
+    rows into a second cache.  Rotating input/output sets keep the 256 MB
+    last-level cache from serving a launch out of the previous one.  Prints
+    one JSON line: appends/s, the roofline of the copy kernel and the oracle's
+    rate on the host."""
+    import numpy as np
+    import torch
+    import block_diffusion_lm_td_amd as td
+    from block_diffusion_lm_td_amd import _td
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[append] generating {w.name}")
+    a = synth.make_attention_inputs(w, args.seed)
+    T, B, S = int(a["total_ctx"]), w.B, w.S
+    N = T + B * S
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    base = {k: up(a[k]) for k in ("k_ctx", "v_ctx", "k_blk", "v_blk")}
+    off = torch.from_numpy(a["offsets"]).to(dev)
+    alg = append_algorithmic(w, T)
+    nsets = args.sets or max(2, int(np.ceil(1.5e9 / alg)))
+    sets = []
+    for i in range(nsets):
+        st = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        k_out = torch.empty((N, w.Hkv, w.D), dtype=st["k_ctx"].dtype, device=dev)
+        o = dict(k_out=k_out, v_out=torch.empty_like(k_out),
+                 off_out=torch.empty((B + 1,), dtype=torch.int64, device=dev))
+        p = td.append_args(st["k_ctx"], st["v_ctx"], off, T, st["k_blk"], st["v_blk"],
+                           o["k_out"], o["v_out"], o["off_out"])
+        sets.append((st, o, p))
+    refs = [ctypes.byref(p) for _, _, p in sets]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    log(f"[append] {nsets} sets, {alg / 1e6:.1f} MB moved per append")
+
+    def run(i):
+        r = L.td_cache_append(refs[i % nsets], sp)
+        if r != 0:
+            raise RuntimeError(_td.status_str(r))
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_back_to_back = t0.elapsed_time(t1) / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        run(i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]))
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    want_off = a["offsets"] + S * np.arange(B + 1)
+    if not np.array_equal(sets[0][1]["off_out"].cpu().numpy(), want_off):
+        raise RuntimeError("td_cache_append wrote unexpected offsets")
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    res = {
+        "metric": "context-cache append: appends/s and % of HBM roofline, 1 GPU",
+        "value": round(1e3 / ms_back_to_back, 2), "unit": "appends/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_append": round(ms_back_to_back, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name + "_append", "B": B, "S_appended": S, "Hkv": w.Hkv, "D": w.D,
+                   "ctx_len": f"uniform integer in [{w.ctx_lo}, {w.ctx_hi}]", "total_ctx": T,
+                   "rows_out": N, "sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "td_cache_append (cache_append_rows)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, APPEND_SRC, APPEND_TRAFFIC_FILE),
+                     "algorithmic_bytes": alg, "avg_launch_us": round(launch_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n, spent = 0, 0.0
+        while spent < args.cpu_budget:
+            c0 = time.perf_counter()
+            oracle.cache_append(a["k_ctx"], a["v_ctx"], a["offsets"], a["k_blk"], a["v_blk"])
+            spent += time.perf_counter() - c0
+            n += 1
+        res["cpu_baseline"] = {"value": round(n / spent, 3), "unit": "appends/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} whole appends of the same cache (numpy "
+                                         f"concatenation, {spent:.1f} s)",
+                               "cpu_model": cpu_model()}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +412,9 @@ def main():
                     help="run --hold-part back-to-back for this many seconds (for sampling board "
                          "power and clocks from outside), print one JSON line and exit")
     ap.add_argument("--hold-part", choices=("step", "attn", "commit"), default="attn")
+    ap.add_argument("--append", action="store_true",
+                    help="time td_cache_append on the workload's cache instead of the step "
+                         "(one JSON line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -308,6 +433,9 @@ def main():
     L = td.lib()
     if args.loop:
         block_loop(args, L)
+        return
+    if args.append:
+        cache_append_bench(args, L)
         return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

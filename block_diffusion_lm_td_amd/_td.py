@@ -34,6 +34,14 @@ class TdCommitArgs(ctypes.Structure):
                 ("n_masked_left", c_void_p)]
 
 
+class TdAppendArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("Hkv", c_int32), ("D", c_int32),
+                ("dtype", c_int), ("k_ctx", c_void_p), ("v_ctx", c_void_p),
+                ("ctx_offsets", c_void_p), ("total_ctx", c_int64), ("k_new", c_void_p),
+                ("v_new", c_void_p), ("k_out", c_void_p), ("v_out", c_void_p),
+                ("offsets_out", c_void_p)]
+
+
 _lib = None
 
 
@@ -45,10 +53,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_diffusion_lm_td_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         A, C = ctypes.POINTER(TdAttnArgs), ctypes.POINTER(TdCommitArgs)
+        P = ctypes.POINTER(TdAppendArgs)
         sig = {
             "td_abi_version": (c_uint32, []),
             "td_sizeof_attn_args": (c_size_t, []),
             "td_sizeof_commit_args": (c_size_t, []),
+            "td_sizeof_append_args": (c_size_t, []),
             "td_status_str": (ctypes.c_char_p, [c_int]),
             "td_attn_workspace_bytes": (c_size_t, [A]),
             "td_commit_workspace_bytes": (c_size_t, [C]),
@@ -57,12 +67,14 @@ def lib() -> ctypes.CDLL:
             "td_commit": (c_int, [C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step": (c_int, [A, C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step_if": (c_int, [A, C, c_void_p, c_void_p, c_size_t, c_void_p]),
+            "td_cache_append": (c_int, [P, c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
         if L.td_sizeof_attn_args() != ctypes.sizeof(TdAttnArgs) or \
-                L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs):
+                L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs) or \
+                L.td_sizeof_append_args() != ctypes.sizeof(TdAppendArgs):
             raise RuntimeError("libtd.so struct layout does not match the binding")
         _lib = L
     return _lib
@@ -162,6 +174,27 @@ def commit_args(logits, commit, token, gamma, masked_in=None, maxprob=None, n_co
     return c
 
 
+def append_args(k_ctx, v_ctx, ctx_offsets, total_ctx, k_new, v_new, k_out, v_out,
+                offsets_out) -> TdAppendArgs:
+    torch = _torch()
+    B, S, Hkv, D = k_new.shape
+    dt = k_new.dtype
+    N = int(total_ctx) + B * S
+    p = TdAppendArgs()
+    p.B, p.S, p.Hkv, p.D = B, S, Hkv, D
+    p.dtype = _dtype_code(k_new)
+    p.k_ctx = _ptr(k_ctx, "k_ctx", dt, (total_ctx, Hkv, D))
+    p.v_ctx = _ptr(v_ctx, "v_ctx", dt, (total_ctx, Hkv, D))
+    p.ctx_offsets = _ptr(ctx_offsets, "ctx_offsets", torch.int64, (B + 1,))
+    p.total_ctx = int(total_ctx)
+    p.k_new = _ptr(k_new, "k_new", dt)
+    p.v_new = _ptr(v_new, "v_new", dt, (B, S, Hkv, D))
+    p.k_out = _ptr(k_out, "k_out", dt, (N, Hkv, D))
+    p.v_out = _ptr(v_out, "v_out", dt, (N, Hkv, D))
+    p.offsets_out = _ptr(offsets_out, "offsets_out", torch.int64, (B + 1,))
+    return p
+
+
 class Workspace:
     """Caller-owned device scratch for the td_* calls (a torch byte tensor,
     grown on demand; torch's allocator returns 256-byte aligned blocks)."""
@@ -237,3 +270,14 @@ def td_denoise_step_if(attn: TdAttnArgs, commit: TdCommitArgs, gate, *, workspac
     ptr, n = _ws(workspace, device).get(need)
     check(L.td_denoise_step_if(ctypes.byref(attn), ctypes.byref(commit), c_void_p(g), ptr, n,
                                _stream(stream)), "td_denoise_step_if")
+
+
+def td_cache_append(k_ctx, v_ctx, ctx_offsets, k_new, v_new, k_out, v_out, offsets_out, *,
+                    total_ctx, stream=None):
+    """Append the block's rows k_new / v_new [B, S, Hkv, D] to every
+    sequence's packed cache: k_out / v_out [total_ctx + B*S, Hkv, D] and
+    offsets_out [B+1] become the next block's context cache."""
+    L = lib()
+    p = append_args(k_ctx, v_ctx, ctx_offsets, total_ctx, k_new, v_new, k_out, v_out, offsets_out)
+    check(L.td_cache_append(ctypes.byref(p), _stream(stream)), "td_cache_append")
+    return k_out, v_out, offsets_out

@@ -1,6 +1,6 @@
 // extern "C" entry points of libtd.so (declared and documented in td.h).
 // Validation and planning happen here, on the host, before anything is
-// enqueued; the launchers live in td_attn.hip / td_commit.hip.
+// enqueued; the launchers live in td_attn.hip / td_commit.hip / td_append.hip.
 #include <stdint.h>
 
 #include "td_internal.h"
@@ -39,6 +39,7 @@ extern "C" {
 uint32_t td_abi_version(void) { return TD_ABI_VERSION; }
 size_t td_sizeof_attn_args(void) { return sizeof(td_attn_args); }
 size_t td_sizeof_commit_args(void) { return sizeof(td_commit_args); }
+size_t td_sizeof_append_args(void) { return sizeof(td_append_args); }
 
 const char *td_status_str(int status) {
   switch (status) {
@@ -93,6 +94,12 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
                        void *ws, size_t ws_bytes, td_stream_t stream) {
   if (!gate || !c || gate == c->n_masked_left) return TD_ERR_INVALID;
   return denoise(a, c, gate, ws, ws_bytes, stream);
+}
+
+int td_cache_append(const td_append_args *p, td_stream_t stream) {
+  const int rc = validate_append(p);
+  if (rc != TD_OK) return rc;
+  return launch_append(p, stream);
 }
 
 }  // extern "C"

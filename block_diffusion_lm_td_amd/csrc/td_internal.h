@@ -44,6 +44,7 @@ struct CommitPlan {
 // Host-side validation and planning (td_plan.cpp): pure functions.
 int validate_attn(const td_attn_args *a, bool check_ptrs);
 int validate_commit(const td_commit_args *c, bool check_ptrs);
+int validate_append(const td_append_args *p);
 AttnPlan plan_attn(const td_attn_args *a);
 CommitPlan plan_commit(const td_commit_args *c);
 
@@ -56,5 +57,6 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                 const int32_t *gate = nullptr);
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
                   const int32_t *gate = nullptr);
+int launch_append(const td_append_args *p, void *stream);
 
 }  // namespace td

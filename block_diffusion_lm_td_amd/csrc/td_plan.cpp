@@ -48,6 +48,55 @@ int validate_commit(const td_commit_args *c, bool check_ptrs) {
   return TD_OK;
 }
 
+namespace {
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi), empty when lo == hi
+};
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+Range range(const void *p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, p ? lo + uintptr_t(bytes) : lo};
+}
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+int validate_append(const td_append_args *p) {
+  if (!p) return TD_ERR_INVALID;
+  if (p->B < 1 || p->S < 0 || p->S > 65536 || p->Hkv < 1 || p->D < 1) return TD_ERR_INVALID;
+  if (p->dtype != TD_F32 && p->dtype != TD_BF16) return TD_ERR_INVALID;
+  if (p->total_ctx < 0) return TD_ERR_INVALID;
+  const int64_t esize = p->dtype == TD_BF16 ? 2 : 4;
+  const int64_t row = int64_t(p->Hkv) * p->D * esize;
+  if (row % 16 != 0 || row > 65536) return TD_ERR_UNSUPPORTED;
+  if (p->B > (1 << 24)) return TD_ERR_UNSUPPORTED;
+  const int64_t n_new = int64_t(p->B) * p->S;
+  const int64_t N = p->total_ctx + n_new;
+  // one workgroup per 16 output rows: the grid stays below 2^31 workgroups
+  if (N > (int64_t(1) << 34) || N * row > (int64_t(1) << 42)) return TD_ERR_UNSUPPORTED;
+  if (!p->ctx_offsets || !p->offsets_out) return TD_ERR_INVALID;
+  if (p->total_ctx > 0 && (!p->k_ctx || !p->v_ctx)) return TD_ERR_INVALID;
+  if (n_new > 0 && (!p->k_new || !p->v_new)) return TD_ERR_INVALID;
+  if (N > 0 && (!p->k_out || !p->v_out)) return TD_ERR_INVALID;
+  for (const void *q : {p->k_ctx, p->v_ctx, p->k_new, p->v_new, (const void *)p->k_out,
+                        (const void *)p->v_out})
+    if (!aligned16(q)) return TD_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(p->ctx_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(p->offsets_out) & 7u) != 0)
+    return TD_ERR_INVALID;
+  const Range ins[] = {range(p->k_ctx, p->total_ctx * row), range(p->v_ctx, p->total_ctx * row),
+                       range(p->k_new, n_new * row), range(p->v_new, n_new * row),
+                       range(p->ctx_offsets, (int64_t(p->B) + 1) * 8)};
+  const Range outs[] = {range(p->k_out, N * row), range(p->v_out, N * row),
+                        range(p->offsets_out, (int64_t(p->B) + 1) * 8)};
+  for (const Range &o : outs)
+    for (const Range &i : ins)
+      if (overlap(o, i)) return TD_ERR_INVALID;
+  for (int x = 0; x < 3; ++x)
+    for (int y = x + 1; y < 3; ++y)
+      if (overlap(outs[x], outs[y])) return TD_ERR_INVALID;
+  return TD_OK;
+}
+
 static int grid_override() {
   const char *env = getenv("TD_ATTN_GRID");
   if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);

@@ -131,10 +131,43 @@ typedef struct {
   int32_t *n_masked_left;  /* out [1] or NULL                                  */
 } td_commit_args;
 
+/*
+ * Context-cache append after a block has committed (chathome, block-generation
+ * paragraph: once a block's positions have all committed, the context tower
+ * takes in the committed tokens and its per-layer KV cache grows by them, so
+ * the next block attends to them as context).  One attention layer's cache:
+ * for every sequence b, with L_b = off[b+1] - off[b],
+ *   off_out[b]         = off[b] + b*S                       (b = 0..B)
+ *   k_out[off_out[b] + j] = k_ctx[off[b] + j]   for j < L_b   (old rows)
+ *   k_out[off_out[b] + L_b + s] = k_new[b, s]   for s < S     (new rows)
+ * and the same for v_out from v_ctx / v_new.  The cache is packed, so the
+ * append is a copy into a second cache (callers alternate two buffers);
+ * k_out and off_out are the next block's k_ctx and ctx_offsets, and the
+ * next block's max_ctx is the old one plus S.
+ */
+typedef struct {
+  int32_t B;               /* sequences, >= 1                                  */
+  int32_t S;               /* rows appended per sequence, 0 .. 65536           */
+  int32_t Hkv, D;          /* >= 1; a row, Hkv*D elements, must be a multiple of
+                              16 bytes (TD_ERR_UNSUPPORTED otherwise)          */
+  td_dtype dtype;          /* element type of every K/V array (copied bitwise) */
+  const void *k_ctx;       /* [total_ctx, Hkv, D] cached keys, packed per seq  */
+  const void *v_ctx;       /* [total_ctx, Hkv, D] cached values                */
+  const int64_t *ctx_offsets; /* DEVICE [B+1]: as in td_attn_args            */
+  int64_t total_ctx;       /* HOST copy of off[B]                              */
+  const void *k_new;       /* [B, S, Hkv, D] the committed tokens' keys (from
+                              the context tower); NULL allowed when S == 0     */
+  const void *v_new;       /* [B, S, Hkv, D] their values                      */
+  void *k_out;             /* out [total_ctx + B*S, Hkv, D]                    */
+  void *v_out;             /* out [total_ctx + B*S, Hkv, D]                    */
+  int64_t *offsets_out;    /* out DEVICE [B+1]                                 */
+} td_append_args;
+
 /* Library identity and struct sizes, for bindings to check their layout. */
 uint32_t td_abi_version(void);
 size_t td_sizeof_attn_args(void);
 size_t td_sizeof_commit_args(void);
+size_t td_sizeof_append_args(void);
 const char *td_status_str(int status);
 
 /* Workspace each call needs, in bytes (0 when none).  Pure host functions:
@@ -175,6 +208,16 @@ int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws,
  * otherwise as td_denoise_step. */
 int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
                        void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* Context-cache append (see td_append_args).  Needs no workspace.  Every
+ * data pointer must be 16-byte aligned; no output may overlap an input or the
+ * other output (k_out/v_out/offsets_out against k_ctx, v_ctx, k_new, v_new,
+ * ctx_offsets): the ranges are checked on the host and TD_ERR_INVALID is
+ * returned for an overlap, a misaligned or missing pointer or a bad size.
+ * Each output row is written exactly once, so inconsistent device offsets give
+ * unspecified values but never an access out of bounds.  Returns a
+ * td_status. */
+int td_cache_append(const td_append_args *p, td_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ def test_struct_layout_and_version(L):
     assert L.td_abi_version() == 1
     assert L.td_sizeof_attn_args() == ctypes.sizeof(_td.TdAttnArgs)
     assert L.td_sizeof_commit_args() == ctypes.sizeof(_td.TdCommitArgs)
+    assert L.td_sizeof_append_args() == ctypes.sizeof(_td.TdAppendArgs)
     for rc in (0, -1, -2, -3, -4, 7):
         assert isinstance(td.status_str(rc), str)
 
@@ -143,3 +144,52 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 16, 4, 64)
     with pytest.raises(ValueError):
         _td.attn_args(x, x, x, x, x, torch.zeros(2, dtype=torch.int64), x, 0, 0)
+
+
+GB = 1 << 32            # distinct fake buffers, far apart: no overlap unless a case makes one
+
+
+def append(**kw):
+    p = _td.TdAppendArgs()
+    p.B, p.S, p.Hkv, p.D, p.dtype = 2, 16, 2, 128, _td.TD_BF16
+    p.total_ctx = 3000
+    p.k_ctx, p.v_ctx, p.k_new, p.v_new = 1 * GB, 2 * GB, 3 * GB, 4 * GB
+    p.k_out, p.v_out = 5 * GB, 6 * GB
+    p.ctx_offsets, p.offsets_out = 7 * GB, 8 * GB
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+ROW = 2 * 128 * 2       # bytes per cache row of the default case
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=0), INVALID), (dict(S=-1), INVALID), (dict(S=65537), INVALID),
+    (dict(Hkv=0), INVALID), (dict(D=0), INVALID), (dict(dtype=7), INVALID),
+    (dict(total_ctx=-1), INVALID),
+    (dict(Hkv=1, D=3), UNSUPPORTED),                          # 6-byte rows
+    (dict(Hkv=256, D=128, dtype=_td.TD_F32), UNSUPPORTED),    # 128 KiB rows
+    (dict(total_ctx=1 << 34, Hkv=1, D=8), UNSUPPORTED),       # more than 2^34 output rows
+    (dict(ctx_offsets=None), INVALID), (dict(offsets_out=None), INVALID),
+    (dict(k_ctx=None), INVALID), (dict(v_new=None), INVALID), (dict(k_out=None), INVALID),
+    (dict(k_ctx=1 * GB + 8), INVALID), (dict(v_out=6 * GB + 4), INVALID),
+    (dict(offsets_out=8 * GB + 4), INVALID),
+    (dict(k_out=1 * GB), INVALID),                            # output on top of its input
+    (dict(v_out=5 * GB + 3031 * ROW), INVALID),               # last row of k_out
+    (dict(k_out=4 * GB + 16 * ROW), INVALID),                 # k_out starts inside v_new
+    (dict(offsets_out=7 * GB + 16), INVALID),                 # offsets_out over ctx_offsets
+    (dict(offsets_out=5 * GB + 64), INVALID),                 # offsets_out inside k_out
+])
+def test_append_validation(L, kw, rc):
+    p = append(**kw)
+    assert L.td_cache_append(ctypes.byref(p), None) == rc
+
+
+def test_append_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(2, 4, 2, 64)
+    with pytest.raises(ValueError):
+        _td.append_args(torch.zeros(0, 2, 64), torch.zeros(0, 2, 64), torch.zeros(3, dtype=torch.int64),
+                        0, x, x, torch.zeros(8, 2, 64), torch.zeros(8, 2, 64),
+                        torch.zeros(3, dtype=torch.int64))

@@ -57,3 +57,11 @@ def test_algorithmic_bytes_of_the_headline_step():
     assert attn_bytes == int(lengths.sum()) * 2 * 512 + w.B * 278528
     assert attn_flops == 4 * w.Hq * w.S * w.D * (int(lengths.sum()) + w.B * w.S)
     assert commit_bytes == w.B * w.S * w.V * 2 + w.B * w.S * 10
+
+
+def test_algorithmic_bytes_of_the_cache_append():
+    import synth
+    w = synth.WORKLOADS["bf16_b64_ragged1k_8k"]
+    # K and V rows of 2 x 128 bf16 (512 B each), read once and written once,
+    # for the 300,000 old rows and the 64 x 16 new ones; offsets read + written
+    assert bench.append_algorithmic(w, 300000) == 4 * (300000 + 1024) * 512 + 16 * 65

@@ -10,4 +10,6 @@ from .td_oracle import (  # noqa: F401
     denoise_step,
     denoise_loop,
     cache_append,
+    lmhead_logits,
+    lmhead_commit,
 )

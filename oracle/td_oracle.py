@@ -171,6 +171,28 @@ def denoise_loop(step_logits, B, S, gamma, max_steps=None):
 
 
 # ----------------------------------------------------------------------------
+# LM head of the block's positions, then the commit ([chathome] block-
+# generation and evaluation paragraphs: every step scores the vocabulary at
+# each block position and commits by confidence)
+# ----------------------------------------------------------------------------
+def lmhead_logits(hidden, w_head):
+    """Vocabulary logits of every block position: the final hidden state
+    hidden [B, S, H] against the LM-head weight w_head [V, H], one row per
+    token id.  Returns logits [B, S, V] in float64."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(w_head, dtype=np.float64)
+    B, S, H = h.shape
+    return (h.reshape(B * S, H) @ w.T).reshape(B, S, w.shape[0])
+
+
+def lmhead_commit(hidden, w_head, masked_in, gamma):
+    """The commit of one step taken straight from the hidden states: the
+    confidence commit over lmhead_logits(hidden, w_head).  Returns the
+    confidence_commit dict."""
+    return confidence_commit(lmhead_logits(hidden, w_head), masked_in, gamma)
+
+
+# ----------------------------------------------------------------------------
 # Context-cache append after a block has committed
 # ([chathome] block-generation paragraph)
 # ----------------------------------------------------------------------------

@@ -7,6 +7,8 @@ oracle consumes the arrays it returns after an exact upcast to float64, the
 HIP path consumes the very same bits on the device.
 """
 from .workloads import (  # noqa: F401
+    LMHEAD_WORKLOADS,
+    LMHeadWorkload,
     WORKLOADS,
     Workload,
     bf16_bits_to_f32,
@@ -14,6 +16,7 @@ from .workloads import (  # noqa: F401
     f32_to_bf16_bits,
     make_attention_inputs,
     make_commit_inputs,
+    make_lmhead_inputs,
     make_eligible,
     loop_step_logits,
     loop_peak_values,

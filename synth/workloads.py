@@ -229,3 +229,66 @@ def loop_step_logits(base: np.ndarray, peak: np.ndarray, stored: np.ndarray, t: 
     x = base.copy()
     x[np.arange(x.shape[0]), peak] = stored[t]
     return x
+
+
+# ----------------------------------------------------------------------------
+# LM head of the block positions: hidden states and head weights
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class LMHeadWorkload:
+    name: str
+    B: int
+    S: int
+    H: int               # hidden size (not on the pages: assumed)
+    V: int               # vocabulary size
+    logit_std: float     # std of the background logits h . w_j (hidden part ~ N(0, 1))
+    margin_hi: float     # planted peak: expected background max + U(0, margin_hi)
+    gamma: float
+
+    def with_(self, **kw) -> "LMHeadWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+LMHEAD_WORKLOADS: dict[str, LMHeadWorkload] = {
+    # Small enough for the oracle on every row: ragged vocabulary and rows.
+    "lmhead_bf16_b4_h256_v5000": LMHeadWorkload(
+        "lmhead_bf16_b4_h256_v5000", B=4, S=16, H=256, V=5000, logit_std=2.0,
+        margin_hi=12.0, gamma=0.8),
+    # The batched step's positions (64 blocks of 16) through a 4096-wide head
+    # over the 131072-entry vocabulary.
+    "lmhead_bf16_b64_h4096_v131072": LMHeadWorkload(
+        "lmhead_bf16_b64_h4096_v131072", B=64, S=16, H=4096, V=131072, logit_std=2.0,
+        margin_hi=12.0, gamma=0.8),
+}
+
+
+def _expected_max_normal(n: int) -> float:
+    """E[max of n standard normals] (the usual asymptotic expansion)."""
+    a = np.sqrt(2.0 * np.log(n))
+    return float(a - (np.log(np.log(n)) + np.log(4.0 * np.pi)) / (2.0 * a))
+
+
+def make_lmhead_inputs(w: LMHeadWorkload, seed: int) -> dict:
+    """hidden [B,S,H] and w_head [V,H] as bf16 bits (uint16).
+
+    w_head ~ N(0, sw^2) with sw = logit_std / sqrt(H), so a random hidden
+    state h ~ N(0, 1) has background logits of std ~logit_std.  Each position
+    gets a planted peak: h = g + c * w_head[t] with a uniform token t and
+    c = (E[max background] + U(0, margin_hi)) / (H sw^2), which lifts token t's
+    logit by about that much above the expected maximum of the others
+    (|w_head[t]|^2 is H sw^2 on average).  Draw order: head, noise, peak ids,
+    margins.
+    """
+    rng = np.random.default_rng([seed, 7])
+    sw = w.logit_std / np.sqrt(w.H)
+    head = _normal(rng, (w.V, w.H), sw)
+    rows = w.B * w.S
+    g = _normal(rng, (rows, w.H), 1.0)
+    peak = rng.integers(0, w.V, size=rows)
+    margin = rng.uniform(0.0, w.margin_hi, size=rows).astype(np.float32)
+    lift = np.float32(w.logit_std * _expected_max_normal(w.V)) + margin
+    c = (lift / np.float32(w.H * sw * sw)).astype(np.float32)
+    g += c[:, None] * head[peak]
+    return dict(hidden=f32_to_bf16_bits(g).reshape(w.B, w.S, w.H),
+                w_head=f32_to_bf16_bits(head), peak=peak, margin=margin, dtype="bf16")
+

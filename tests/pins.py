@@ -565,3 +565,97 @@ def pin_append_then_attend(append):
 APPEND_PINS = [pin_append_time_order, pin_append_offsets_closed_form, pin_append_identities,
                pin_append_two_blocks_at_once, pin_append_then_attend]
 
+
+# ----------------------------------------------------------------------------
+# LM-head pins ([chathome] block-generation and evaluation paragraphs)
+# ----------------------------------------------------------------------------
+def pin_lmhead_logits_torch(logits_fn):
+    """Against torch's float64 linear layer (a different library routine)."""
+    rng = np.random.default_rng(51)
+    h = rng.standard_normal((2, 3, 40))
+    w = rng.standard_normal((50, 40))
+    want = torch.nn.functional.linear(torch.from_numpy(h), torch.from_numpy(w)).numpy()
+    _close(logits_fn(h, w), want, tol=1e-12, what="logits vs torch linear")
+
+
+def pin_lmhead_logits_brute(logits_fn):
+    """Pure-Python sums on a tiny case, token j's logit = sum_k h_k w[j]_k."""
+    rng = np.random.default_rng(52)
+    h = rng.integers(-3, 4, (1, 2, 5)).astype(np.float64)
+    w = rng.integers(-3, 4, (4, 5)).astype(np.float64)
+    got = np.asarray(logits_fn(h, w))
+    assert got.shape == (1, 2, 4)
+    for i in range(2):
+        for j in range(4):
+            assert got[0, i, j] == sum(h[0, i, k] * w[j, k] for k in range(5)), (i, j)
+
+
+def pin_lmhead_identity_head(lmc):
+    """With H = V and the identity as LM head, the hidden state is the logit
+    row: the hand-derived commit fixture must come out."""
+    with open(os.path.join(GOLDEN, "commit_closed_form.json")) as f:
+        g = json.load(f)
+    x = np.array(g["logits"], dtype=np.float64)
+    eye = np.eye(x.shape[-1])
+    for case in g["cases"]:
+        r = lmc(x, eye, np.array(case["eligible"], dtype=np.uint8), case["gamma"])
+        assert np.asarray(r["commit"]).astype(int).tolist() == case["commit"], case["name"]
+        assert np.asarray(r["token"]).tolist() == g["token"], case["name"]
+        assert np.asarray(r["n_commit"]).tolist() == case["n_commit"], case["name"]
+        _close(r["maxprob"], np.array(g["maxprob"]), tol=1e-15, what=case["name"])
+
+
+def _int_head(seed, B=2, S=4, H=6, V=9):
+    rng = np.random.default_rng(seed)
+    h = rng.integers(-2, 3, (B, S, H)).astype(np.float64)
+    w = rng.integers(-2, 3, (V, H)).astype(np.float64)
+    m = rng.integers(0, 2, (B, S)).astype(np.uint8)
+    m[:, 0] = 1
+    return h, w, m
+
+
+def pin_lmhead_shift_invariance(lmc):
+    """Adding one vector c to every row of the head adds h.c to all logits of
+    a position: softmax, argmax and so every decision stay the same (integer
+    data keeps this exact)."""
+    h, w, m = _int_head(53)
+    c = np.array([1.0, -2.0, 0.0, 3.0, 1.0, -1.0])
+    for gamma in (0.3, 0.6):
+        a = lmc(h, w, m, gamma)
+        b = lmc(h, w + c, m, gamma)
+        for k in ("commit", "token", "n_commit"):
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+        _close(a["maxprob"], b["maxprob"], tol=1e-15, what="maxprob under a shift")
+
+
+def pin_lmhead_vocab_permutation(lmc):
+    """Renumbering the vocabulary (rows of the head) renumbers the argmax and
+    leaves the probabilities and the commit decisions unchanged."""
+    rng = np.random.default_rng(54)
+    h = rng.standard_normal((2, 4, 8))
+    w = rng.standard_normal((11, 8))
+    m = np.array([[1, 1, 0, 1], [0, 1, 1, 1]], np.uint8)
+    perm = rng.permutation(11)                  # new id k is old token perm[k]
+    a = lmc(h, w, m, 0.35)
+    b = lmc(h, w[perm], m, 0.35)
+    assert np.array_equal(perm[np.asarray(b["token"])], np.asarray(a["token"]))
+    assert np.array_equal(np.asarray(a["commit"]), np.asarray(b["commit"]))
+    _close(a["maxprob"], b["maxprob"], tol=1e-14, what="maxprob under renumbering")
+
+
+def pin_lmhead_eligibility(lmc):
+    """Ineligible positions never commit, and a sequence with no eligible
+    position commits nothing; the force-one rule still applies per
+    sequence."""
+    h, w, _ = _int_head(55)
+    m = np.array([[0, 0, 0, 0], [0, 0, 1, 0]], np.uint8)
+    r = lmc(h, w, m, 2.0)                          # gamma > 1: force-one only
+    c = np.asarray(r["commit"]).astype(bool)
+    assert not c[0].any() and c[1].tolist() == [False, False, True, False]
+    assert np.asarray(r["n_commit"]).tolist() == [0, 1]
+
+
+LMHEAD_LOGIT_PINS = [pin_lmhead_logits_torch, pin_lmhead_logits_brute]
+LMHEAD_PINS = [pin_lmhead_identity_head, pin_lmhead_shift_invariance, pin_lmhead_vocab_permutation,
+               pin_lmhead_eligibility]
+

@@ -33,3 +33,13 @@ def test_step_pin(pin):
 @pytest.mark.parametrize("pin", pins.APPEND_PINS, ids=lambda f: f.__name__)
 def test_append_pin(pin):
     pin(oracle.cache_append)
+
+
+@pytest.mark.parametrize("pin", pins.LMHEAD_LOGIT_PINS, ids=lambda f: f.__name__)
+def test_lmhead_logits_pin(pin):
+    pin(oracle.lmhead_logits)
+
+
+@pytest.mark.parametrize("pin", pins.LMHEAD_PINS, ids=lambda f: f.__name__)
+def test_lmhead_commit_pin(pin):
+    pin(oracle.lmhead_commit)

@@ -47,6 +47,14 @@ MUTANTS = [
      "offsets_out[b] + (stop - start)"),
     ("append_drops_last_old_row", "k_ctx[start:stop], k_new[b]", "k_ctx[start:stop - 1], k_new[b]"),
     ("append_neighbours_rows", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b - 1]]"),
+    ("lmhead_vocab_reversed", "(h.reshape(B * S, H) @ w.T)", "(h.reshape(B * S, H) @ w[::-1].T)"),
+    ("lmhead_negated", "(h.reshape(B * S, H) @ w.T)", "(h.reshape(B * S, H) @ -w.T)"),
+    ("lmhead_rows_transposed", "(h.reshape(B * S, H) @ w.T)",
+     "(h.transpose(1, 0, 2).reshape(B * S, H) @ w.T)"),
+    ("lmhead_drops_eligibility", "confidence_commit(lmhead_logits(hidden, w_head), masked_in, gamma)",
+     "confidence_commit(lmhead_logits(hidden, w_head), None, gamma)"),
+    ("lmhead_last_hidden_unit_dropped", "(h.reshape(B * S, H) @ w.T)",
+     "(h[..., :-1].reshape(B * S, H - 1) @ w[:, :-1].T)"),
     ("append_new_rows_truncated", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b, 1:]]"),
 ]
 
@@ -67,6 +75,8 @@ def _all_pins(mod):
     yield from ((p, mod.denoise_loop) for p in pins.LOOP_PINS)
     yield from ((p, mod.denoise_step) for p in pins.STEP_PINS)
     yield from ((p, mod.cache_append) for p in pins.APPEND_PINS)
+    yield from ((p, mod.lmhead_logits) for p in pins.LMHEAD_LOGIT_PINS)
+    yield from ((p, mod.lmhead_commit) for p in pins.LMHEAD_PINS)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

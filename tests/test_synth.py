@@ -55,3 +55,17 @@ def test_loop_logits_peak_grows():
     assert (x2[np.arange(x2.shape[0]), peak] == stored[2]).all()
     x0 = synth.loop_step_logits(base, peak, stored, 0)
     assert (x0 == base).all()
+
+
+def test_lmhead_inputs_deterministic_and_shaped():
+    w = synth.LMHEAD_WORKLOADS["lmhead_bf16_b4_h256_v5000"]
+    a = synth.make_lmhead_inputs(w, 11)
+    b = synth.make_lmhead_inputs(w, 11)
+    assert a["hidden"].shape == (4, 16, 256) and a["hidden"].dtype == np.uint16
+    assert a["w_head"].shape == (5000, 256) and a["w_head"].dtype == np.uint16
+    assert np.array_equal(a["hidden"], b["hidden"]) and np.array_equal(a["w_head"], b["w_head"])
+    c = synth.make_lmhead_inputs(w, 12)
+    assert not np.array_equal(a["w_head"], c["w_head"])
+    # the head's spread: sw = logit_std / sqrt(H)
+    sw = synth.bf16_bits_to_f64(a["w_head"]).std()
+    assert abs(sw - 2.0 / 16.0) < 0.005

@@ -8,11 +8,13 @@ from ._td import (  # noqa: F401
     TdAppendArgs,
     TdAttnArgs,
     TdCommitArgs,
+    TdLmheadArgs,
     Workspace,
     append_args,
     attn_args,
     commit_args,
     header_functions,
+    lmhead_args,
     lib,
     status_str,
     td_block_attn,
@@ -20,4 +22,5 @@ from ._td import (  # noqa: F401
     td_commit,
     td_denoise_step,
     td_denoise_step_if,
+    td_lmhead_commit,
 )

@@ -42,6 +42,14 @@ class TdAppendArgs(ctypes.Structure):
                 ("offsets_out", c_void_p)]
 
 
+class TdLmheadArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("H", c_int32), ("V", c_int32),
+                ("dtype", c_int), ("gamma", c_float), ("hidden", c_void_p), ("w_head", c_void_p),
+                ("masked_in", c_void_p), ("commit", c_void_p), ("token", c_void_p),
+                ("maxprob", c_void_p), ("n_commit", c_void_p), ("masked_out", c_void_p),
+                ("tokens", c_void_p), ("n_masked_left", c_void_p)]
+
+
 _lib = None
 
 
@@ -54,11 +62,13 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         A, C = ctypes.POINTER(TdAttnArgs), ctypes.POINTER(TdCommitArgs)
         P = ctypes.POINTER(TdAppendArgs)
+        LH = ctypes.POINTER(TdLmheadArgs)
         sig = {
             "td_abi_version": (c_uint32, []),
             "td_sizeof_attn_args": (c_size_t, []),
             "td_sizeof_commit_args": (c_size_t, []),
             "td_sizeof_append_args": (c_size_t, []),
+            "td_sizeof_lmhead_args": (c_size_t, []),
             "td_status_str": (ctypes.c_char_p, [c_int]),
             "td_attn_workspace_bytes": (c_size_t, [A]),
             "td_commit_workspace_bytes": (c_size_t, [C]),
@@ -68,13 +78,16 @@ def lib() -> ctypes.CDLL:
             "td_denoise_step": (c_int, [A, C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step_if": (c_int, [A, C, c_void_p, c_void_p, c_size_t, c_void_p]),
             "td_cache_append": (c_int, [P, c_void_p]),
+            "td_lmhead_commit_workspace_bytes": (c_size_t, [LH]),
+            "td_lmhead_commit": (c_int, [LH, c_void_p, c_size_t, c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
         if L.td_sizeof_attn_args() != ctypes.sizeof(TdAttnArgs) or \
                 L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs) or \
-                L.td_sizeof_append_args() != ctypes.sizeof(TdAppendArgs):
+                L.td_sizeof_append_args() != ctypes.sizeof(TdAppendArgs) or \
+                L.td_sizeof_lmhead_args() != ctypes.sizeof(TdLmheadArgs):
             raise RuntimeError("libtd.so struct layout does not match the binding")
         _lib = L
     return _lib
@@ -195,6 +208,28 @@ def append_args(k_ctx, v_ctx, ctx_offsets, total_ctx, k_new, v_new, k_out, v_out
     return p
 
 
+def lmhead_args(hidden, w_head, commit, token, gamma, masked_in=None, maxprob=None,
+                n_commit=None, masked_out=None, tokens=None, n_masked_left=None) -> TdLmheadArgs:
+    torch = _torch()
+    B, S, H = hidden.shape
+    V = w_head.shape[0]
+    a = TdLmheadArgs()
+    a.B, a.S, a.H, a.V = B, S, H, V
+    a.dtype = _dtype_code(hidden)
+    a.gamma = float(gamma)
+    a.hidden = _ptr(hidden, "hidden")
+    a.w_head = _ptr(w_head, "w_head", hidden.dtype, (V, H))
+    a.masked_in = _ptr(masked_in, "masked_in", torch.uint8, (B, S))
+    a.commit = _ptr(commit, "commit", torch.uint8, (B, S))
+    a.token = _ptr(token, "token", torch.int32, (B, S))
+    a.maxprob = _ptr(maxprob, "maxprob", torch.float32, (B, S))
+    a.n_commit = _ptr(n_commit, "n_commit", torch.int32, (B,))
+    a.masked_out = _ptr(masked_out, "masked_out", torch.uint8, (B, S))
+    a.tokens = _ptr(tokens, "tokens", torch.int32, (B, S))
+    a.n_masked_left = _ptr(n_masked_left, "n_masked_left", torch.int32, (1,))
+    return a
+
+
 class Workspace:
     """Caller-owned device scratch for the td_* calls (a torch byte tensor,
     grown on demand; torch's allocator returns 256-byte aligned blocks)."""
@@ -281,3 +316,17 @@ def td_cache_append(k_ctx, v_ctx, ctx_offsets, k_new, v_new, k_out, v_out, offse
     p = append_args(k_ctx, v_ctx, ctx_offsets, total_ctx, k_new, v_new, k_out, v_out, offsets_out)
     check(L.td_cache_append(ctypes.byref(p), _stream(stream)), "td_cache_append")
     return k_out, v_out, offsets_out
+
+
+def td_lmhead_commit(hidden, w_head, commit, token, *, gamma, masked_in=None, maxprob=None,
+                     n_commit=None, masked_out=None, tokens=None, n_masked_left=None,
+                     workspace=None, stream=None):
+    """Commit of one step straight from the block's hidden states [B, S, H]
+    and the LM-head weight [V, H]: the logits stay on chip."""
+    L = lib()
+    a = lmhead_args(hidden, w_head, commit, token, gamma, masked_in, maxprob, n_commit,
+                    masked_out, tokens, n_masked_left)
+    need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
+    ptr, n = _ws(workspace, hidden.device).get(need)
+    check(L.td_lmhead_commit(ctypes.byref(a), ptr, n, _stream(stream)), "td_lmhead_commit")
+

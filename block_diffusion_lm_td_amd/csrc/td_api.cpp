@@ -1,6 +1,7 @@
 // extern "C" entry points of libtd.so (declared and documented in td.h).
 // Validation and planning happen here, on the host, before anything is
-// enqueued; the launchers live in td_attn.hip / td_commit.hip / td_append.hip.
+// enqueued; the launchers live in td_attn.hip / td_commit.hip / td_lmhead.hip /
+// td_append.hip.
 #include <stdint.h>
 
 #include "td_internal.h"
@@ -40,6 +41,7 @@ uint32_t td_abi_version(void) { return TD_ABI_VERSION; }
 size_t td_sizeof_attn_args(void) { return sizeof(td_attn_args); }
 size_t td_sizeof_commit_args(void) { return sizeof(td_commit_args); }
 size_t td_sizeof_append_args(void) { return sizeof(td_append_args); }
+size_t td_sizeof_lmhead_args(void) { return sizeof(td_lmhead_args); }
 
 const char *td_status_str(int status) {
   switch (status) {
@@ -65,6 +67,11 @@ size_t td_commit_workspace_bytes(const td_commit_args *c) {
 size_t td_denoise_workspace_bytes(const td_attn_args *a, const td_commit_args *c) {
   if (validate_attn(a, false) != TD_OK || validate_commit(c, false) != TD_OK) return 0;
   return align256(plan_attn(a).ws_bytes) + align256(plan_commit(c).ws_bytes);
+}
+
+size_t td_lmhead_commit_workspace_bytes(const td_lmhead_args *a) {
+  if (validate_lmhead(a, false) != TD_OK) return 0;
+  return lmhead_ws_bytes(a);
 }
 
 int td_block_attn(const td_attn_args *a, void *ws, size_t ws_bytes, td_stream_t stream) {
@@ -94,6 +101,14 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
                        void *ws, size_t ws_bytes, td_stream_t stream) {
   if (!gate || !c || gate == c->n_masked_left) return TD_ERR_INVALID;
   return denoise(a, c, gate, ws, ws_bytes, stream);
+}
+
+int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stream_t stream) {
+  int rc = validate_lmhead(a, true);
+  if (rc != TD_OK) return rc;
+  rc = check_ws(lmhead_ws_bytes(a), ws, ws_bytes);
+  if (rc != TD_OK) return rc;
+  return launch_lmhead(a, ws, stream);
 }
 
 int td_cache_append(const td_append_args *p, td_stream_t stream) {

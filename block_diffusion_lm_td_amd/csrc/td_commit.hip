@@ -40,13 +40,6 @@ __device__ inline float4 ldv(const float4 *p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-struct Part {
-  float m;    // max of the part
-  float z;    // sum exp(x - m) over the part
-  int idx;    // lowest index attaining m
-  int pad;
-};
-
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline void unpack(const uint4 &v, float (&f)[8]) {
@@ -238,6 +231,17 @@ __global__ __launch_bounds__(64) void commit_finalize(
 
 }  // namespace
 
+int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,
+                           const uint8_t *masked_in, uint8_t *commit, int32_t *token,
+                           float *maxprob, int32_t *n_commit, uint8_t *masked_out,
+                           int32_t *tokens, int32_t *n_masked_left, void *stream,
+                           const int32_t *gate) {
+  hipLaunchKernelGGL(commit_finalize, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                     parts, S, R, gamma, masked_in, commit, token, maxprob, n_commit, masked_out,
+                     tokens, n_masked_left, gate);
+  return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
+}
+
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
                   const int32_t *gate) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -258,10 +262,10 @@ int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *
       hipLaunchKernelGGL((commit_rows<float, false>), dim3(nblk), dim3(256), 0, st,
                          static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
   }
-  hipLaunchKernelGGL(commit_finalize, dim3(c->B), dim3(64), 0, st, parts, c->S, p.R, c->gamma,
-                     c->masked_in, c->commit, c->token, c->maxprob, c->n_commit, c->masked_out,
-                     c->tokens, c->n_masked_left, gate);
-  return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return TD_ERR_HIP;
+  return launch_commit_finalize(parts, p.R, c->B, c->S, c->gamma, c->masked_in, c->commit, c->token,
+                                c->maxprob, c->n_commit, c->masked_out, c->tokens,
+                                c->n_masked_left, stream, gate);
 }
 
 }  // namespace td

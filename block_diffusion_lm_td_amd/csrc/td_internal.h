@@ -16,6 +16,14 @@ constexpr int kWaves = 8;         // 8 waves x 32 rows; two waves share each SIM
 constexpr int kWGThreads = 64 * kWaves;
 constexpr int kGridWGs = 256;     // persistent grid: one workgroup per CU of MI355X
 
+// Partial of the commit's vocabulary pass over one part of a row (16 bytes).
+struct Part {
+  float m;    // max of the part
+  float z;    // sum exp(x - m) over the part
+  int idx;    // lowest index attaining m
+  int pad;
+};
+
 // Launch plan of one td_block_attn call, derived on the host from sizes only.
 struct AttnPlan {
   bool mfma;            // bf16, D == 128: MFMA kernel; otherwise the VALU kernel
@@ -45,6 +53,7 @@ struct CommitPlan {
 int validate_attn(const td_attn_args *a, bool check_ptrs);
 int validate_commit(const td_commit_args *c, bool check_ptrs);
 int validate_append(const td_append_args *p);
+int validate_lmhead(const td_lmhead_args *a, bool check_ptrs);
 AttnPlan plan_attn(const td_attn_args *a);
 CommitPlan plan_commit(const td_commit_args *c);
 
@@ -58,5 +67,18 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
                   const int32_t *gate = nullptr);
 int launch_append(const td_append_args *p, void *stream);
+// the commit's per-sequence decision over R parts per position (td_commit.hip)
+int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,
+                           const uint8_t *masked_in, uint8_t *commit, int32_t *token,
+                           float *maxprob, int32_t *n_commit, uint8_t *masked_out,
+                           int32_t *tokens, int32_t *n_masked_left, void *stream,
+                           const int32_t *gate = nullptr);
+// fused LM head + commit (td_lmhead.hip): workspace = parts, then one merged
+// part per position
+size_t lmhead_parts_bytes(const td_lmhead_args *a);
+inline size_t lmhead_ws_bytes(const td_lmhead_args *a) {
+  return align256(lmhead_parts_bytes(a)) + size_t(a->B) * a->S * sizeof(Part);
+}
+int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream);
 
 }  // namespace td

@@ -163,11 +163,42 @@ typedef struct {
   int64_t *offsets_out;    /* out DEVICE [B+1]                                 */
 } td_append_args;
 
+/*
+ * LM head of the block positions fused with the commit (chathome,
+ * block-generation and evaluation paragraphs: each denoising step scores the
+ * vocabulary at every block position, then commits by confidence).  For
+ * every position (b, i):
+ *   logits[b,i,j] = sum_k hidden[b,i,k] * w_head[j,k]     (j = 0 .. V-1)
+ * computed in fp32 from bf16 operands and never written to memory; then the
+ * commit of td_commit_args over those logits (same outputs, same rules:
+ * token = lowest argmax, maxprob = 1 / sum_j exp(logits - max), threshold
+ * p >= gamma on the eligible positions, force-one).
+ */
+typedef struct {
+  int32_t B;               /* >= 1                                             */
+  int32_t S;               /* 1 .. 64                                          */
+  int32_t H;               /* hidden size: a multiple of 32, 32 .. 65536       */
+  int32_t V;               /* vocabulary size, 1 .. 2^30                       */
+  td_dtype dtype;          /* TD_BF16 (TD_ERR_UNSUPPORTED otherwise)           */
+  float gamma;             /* confidence threshold, finite                     */
+  const void *hidden;      /* [B, S, H] final hidden state of each position    */
+  const void *w_head;      /* [V, H] LM-head weight, row j = token j            */
+  const uint8_t *masked_in;/* [B, S] 1 = still [MASK] (eligible); NULL = all   */
+  uint8_t *commit;         /* out [B, S]                                       */
+  int32_t *token;          /* out [B, S]  argmax id at EVERY position          */
+  float *maxprob;          /* out [B, S] or NULL                               */
+  int32_t *n_commit;       /* out [B] or NULL                                  */
+  uint8_t *masked_out;     /* out [B, S] or NULL; may alias masked_in          */
+  int32_t *tokens;         /* in/out [B, S] or NULL: ids written where committed */
+  int32_t *n_masked_left;  /* out [1] or NULL                                  */
+} td_lmhead_args;
+
 /* Library identity and struct sizes, for bindings to check their layout. */
 uint32_t td_abi_version(void);
 size_t td_sizeof_attn_args(void);
 size_t td_sizeof_commit_args(void);
 size_t td_sizeof_append_args(void);
+size_t td_sizeof_lmhead_args(void);
 const char *td_status_str(int status);
 
 /* Workspace each call needs, in bytes (0 when none).  Pure host functions:
@@ -176,6 +207,7 @@ const char *td_status_str(int status);
 size_t td_attn_workspace_bytes(const td_attn_args *a);
 size_t td_commit_workspace_bytes(const td_commit_args *c);
 size_t td_denoise_workspace_bytes(const td_attn_args *a, const td_commit_args *c);
+size_t td_lmhead_commit_workspace_bytes(const td_lmhead_args *a);
 
 /* Block attention (see td_attn_args).  Returns a td_status. */
 int td_block_attn(const td_attn_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
@@ -208,6 +240,12 @@ int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws,
  * otherwise as td_denoise_step. */
 int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
                        void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* Fused LM head + commit (see td_lmhead_args).  hidden and w_head must be
+ * 16-byte aligned.  The workspace (td_lmhead_commit_workspace_bytes) holds
+ * 16 bytes per (position, 256-token slice of the vocabulary).  Returns a
+ * td_status. */
+int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
 
 /* Context-cache append (see td_append_args).  Needs no workspace.  Every
  * data pointer must be 16-byte aligned; no output may overlap an input or the

@@ -244,6 +244,7 @@ class LMHeadWorkload:
     logit_std: float     # std of the background logits h . w_j (hidden part ~ N(0, 1))
     margin_hi: float     # planted peak: expected background max + U(0, margin_hi)
     gamma: float
+    exact: bool = False  # values on grids that make every fp32 partial sum exact
 
     def with_(self, **kw) -> "LMHeadWorkload":
         return dataclasses.replace(self, **kw)
@@ -254,6 +255,10 @@ LMHEAD_WORKLOADS: dict[str, LMHeadWorkload] = {
     "lmhead_bf16_b4_h256_v5000": LMHeadWorkload(
         "lmhead_bf16_b4_h256_v5000", B=4, S=16, H=256, V=5000, logit_std=2.0,
         margin_hi=12.0, gamma=0.8),
+    # The same with exactly representable sums (see make_lmhead_inputs).
+    "lmhead_exact_b4_h256_v5000": LMHeadWorkload(
+        "lmhead_exact_b4_h256_v5000", B=4, S=16, H=256, V=5000, logit_std=2.0,
+        margin_hi=12.0, gamma=0.8, exact=True),
     # The batched step's positions (64 blocks of 16) through a 4096-wide head
     # over the 131072-entry vocabulary.
     "lmhead_bf16_b64_h4096_v131072": LMHeadWorkload(
@@ -263,7 +268,9 @@ LMHEAD_WORKLOADS: dict[str, LMHeadWorkload] = {
 
 
 def _expected_max_normal(n: int) -> float:
-    """E[max of n standard normals] (the usual asymptotic expansion)."""
+    """E[max of n standard normals] (the usual asymptotic expansion; 0 for n < 2)."""
+    if n < 2:
+        return 0.0
     a = np.sqrt(2.0 * np.log(n))
     return float(a - (np.log(np.log(n)) + np.log(4.0 * np.pi)) / (2.0 * a))
 
@@ -278,6 +285,12 @@ def make_lmhead_inputs(w: LMHeadWorkload, seed: int) -> dict:
     logit by about that much above the expected maximum of the others
     (|w_head[t]|^2 is H sw^2 on average).  Draw order: head, noise, peak ids,
     margins.
+
+    ``exact``: hidden values are rounded to multiples of 1/4 in [-8, 8] and
+    head values to multiples of 1/256 in [-1/8, 1/8].  Every product is then a
+    multiple of 2^-10 of magnitude <= 1, so every partial sum of up to 4096
+    products is a multiple of 2^-10 below 2^12 in magnitude: 22 significant
+    bits, exact in float32 in any summation order.
     """
     rng = np.random.default_rng([seed, 7])
     sw = w.logit_std / np.sqrt(w.H)
@@ -289,6 +302,10 @@ def make_lmhead_inputs(w: LMHeadWorkload, seed: int) -> dict:
     lift = np.float32(w.logit_std * _expected_max_normal(w.V)) + margin
     c = (lift / np.float32(w.H * sw * sw)).astype(np.float32)
     g += c[:, None] * head[peak]
+    if w.exact:
+        assert w.H <= 4096
+        head = np.clip(np.rint(head * 256.0), -32.0, 32.0).astype(np.float32) / np.float32(256.0)
+        g = np.clip(np.rint(g * 4.0), -32.0, 32.0).astype(np.float32) / np.float32(4.0)
     return dict(hidden=f32_to_bf16_bits(g).reshape(w.B, w.S, w.H),
                 w_head=f32_to_bf16_bits(head), peak=peak, margin=margin, dtype="bf16")
 

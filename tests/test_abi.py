@@ -30,6 +30,7 @@ def test_struct_layout_and_version(L):
     assert L.td_sizeof_attn_args() == ctypes.sizeof(_td.TdAttnArgs)
     assert L.td_sizeof_commit_args() == ctypes.sizeof(_td.TdCommitArgs)
     assert L.td_sizeof_append_args() == ctypes.sizeof(_td.TdAppendArgs)
+    assert L.td_sizeof_lmhead_args() == ctypes.sizeof(_td.TdLmheadArgs)
     for rc in (0, -1, -2, -3, -4, 7):
         assert isinstance(td.status_str(rc), str)
 
@@ -193,3 +194,37 @@ def test_append_binding_rejects_host_tensors():
         _td.append_args(torch.zeros(0, 2, 64), torch.zeros(0, 2, 64), torch.zeros(3, dtype=torch.int64),
                         0, x, x, torch.zeros(8, 2, 64), torch.zeros(8, 2, 64),
                         torch.zeros(3, dtype=torch.int64))
+
+
+def lmhead(**kw):
+    a = _td.TdLmheadArgs()
+    a.B, a.S, a.H, a.V, a.dtype, a.gamma = 64, 16, 4096, 131072, _td.TD_BF16, 0.8
+    a.hidden, a.w_head, a.commit, a.token = 1 * GB, 2 * GB, 3 * GB, 4 * GB
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(S=65), INVALID), (dict(V=0), INVALID),
+    (dict(H=0), INVALID), (dict(dtype=7), INVALID), (dict(gamma=float("inf")), INVALID),
+    (dict(dtype=_td.TD_F32), UNSUPPORTED), (dict(H=100), UNSUPPORTED), (dict(H=65568), UNSUPPORTED),
+    (dict(hidden=None), INVALID), (dict(w_head=None), INVALID), (dict(commit=None), INVALID),
+    (dict(token=None), INVALID), (dict(hidden=1 * GB + 2), INVALID), (dict(w_head=2 * GB + 8), INVALID),
+])
+def test_lmhead_validation(L, kw, rc):
+    a = lmhead(**kw)
+    assert L.td_lmhead_commit(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == rc
+
+
+def test_lmhead_workspace_bytes(L):
+    """16 bytes per (position, 256-token slice), then 16 per position."""
+    a = lmhead()
+    parts = 64 * 16 * 512 * 16
+    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(a)) == parts + 64 * 16 * 16
+    b = lmhead(V=257, B=1, S=3)
+    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(b)) == 256 + 3 * 16
+    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(lmhead(H=100))) == 0
+    need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
+    assert L.td_lmhead_commit(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+

@@ -37,7 +37,7 @@ def _instructions(lines):
     return [ln for ln in lines if ln and not ln.startswith(".") and not ln.endswith(":")]
 
 
-@pytest.mark.parametrize("name", ["td_attn.hip", "td_commit.hip"])
+@pytest.mark.parametrize("name", ["td_attn.hip", "td_commit.hip", "td_lmhead.hip", "td_append.hip"])
 def test_m0_only_feeds_the_tile_dma(name, tmp_path):
     ins = _instructions(_asm(name, tmp_path))
     uses = [i for i, s in enumerate(ins) if re.search(r"\bm0\b", s)]
@@ -46,6 +46,6 @@ def test_m0_only_feeds_the_tile_dma(name, tmp_path):
         assert re.fullmatch(r"s_mov_b32 m0, s\d+", s), f"M0 used outside the DMA pattern: {s!r}"
         assert ins[i + 1].startswith("global_load_lds_dwordx4"), \
             f"M0 write not followed by the DMA: {s!r} then {ins[i + 1]!r}"
-    if name == "td_attn.hip":
-        assert uses, "the attention kernel should contain the tile DMA"
+    if name in ("td_attn.hip", "td_lmhead.hip"):
+        assert uses, f"{name} should contain the tile DMA"
 

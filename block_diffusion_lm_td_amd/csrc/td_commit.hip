@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64) void commit_finalize(
     const Part *__restrict__ parts, int S, int R, float gamma, const uint8_t *masked_in,
     uint8_t *__restrict__ commit, int32_t *__restrict__ token, float *__restrict__ maxprob,
     int32_t *__restrict__ n_commit, uint8_t *masked_out, int32_t *__restrict__ tokens,
-    int32_t *__restrict__ n_masked_left, const int32_t *__restrict__ gate) {
+    int32_t *__restrict__ n_masked_left, const int32_t *__restrict__ gate, bool skip_inelig) {
   if (gate && *gate == 0) return;
   const int b = blockIdx.x;
   const int i = threadIdx.x;
@@ -185,7 +185,10 @@ __global__ __launch_bounds__(64) void commit_finalize(
   float p = 0.f;
   int idx = 0;
   bool elig = false;
-  if (act) {
+  if (act) elig = masked_in ? masked_in[row] != 0 : true;
+  if (act && skip_inelig && !elig) {
+    idx = -1;                        // not scored: no parts were made for it
+  } else if (act) {
     float M = kNegInf;
     for (int r = 0; r < R; ++r) M = fmaxf(M, parts[row * R + r].m);
     float Z = 0.f;
@@ -196,7 +199,6 @@ __global__ __launch_bounds__(64) void commit_finalize(
       Z += (q.m == kNegInf) ? 0.f : q.z * fast_exp2((q.m - M) * kLog2e);
     }
     p = 1.0f / Z;
-    elig = masked_in ? masked_in[row] != 0 : true;
   }
   const bool pass = act && elig && p >= gamma;
   const unsigned long long pm = __ballot(pass);
@@ -235,10 +237,10 @@ int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,
                            const uint8_t *masked_in, uint8_t *commit, int32_t *token,
                            float *maxprob, int32_t *n_commit, uint8_t *masked_out,
                            int32_t *tokens, int32_t *n_masked_left, void *stream,
-                           const int32_t *gate) {
+                           const int32_t *gate, bool skip_ineligible) {
   hipLaunchKernelGGL(commit_finalize, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
                      parts, S, R, gamma, masked_in, commit, token, maxprob, n_commit, masked_out,
-                     tokens, n_masked_left, gate);
+                     tokens, n_masked_left, gate, skip_ineligible);
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }
 

@@ -72,12 +72,13 @@ int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,
                            const uint8_t *masked_in, uint8_t *commit, int32_t *token,
                            float *maxprob, int32_t *n_commit, uint8_t *masked_out,
                            int32_t *tokens, int32_t *n_masked_left, void *stream,
-                           const int32_t *gate = nullptr);
-// fused LM head + commit (td_lmhead.hip): workspace = parts, then one merged
-// part per position
+                           const int32_t *gate = nullptr, bool skip_ineligible = false);
+// fused LM head + commit (td_lmhead.hip): workspace = parts, one merged part
+// per position, then the compacted position list and its count
 size_t lmhead_parts_bytes(const td_lmhead_args *a);
 inline size_t lmhead_ws_bytes(const td_lmhead_args *a) {
-  return align256(lmhead_parts_bytes(a)) + size_t(a->B) * a->S * sizeof(Part);
+  const size_t M = size_t(a->B) * a->S;
+  return align256(lmhead_parts_bytes(a)) + align256(M * sizeof(Part)) + (M + 1) * sizeof(int32_t);
 }
 int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream);
 

@@ -9,17 +9,23 @@
 //   each position's 256 logits of the tile to (max, lowest argmax, sum of
 //   exp(x - max)), the same partial the commit's vocabulary pass produces,
 //   and writes 16 bytes per (position, tile) instead of 512.
-//   - Operands stream through a 4-stage LDS ring of 32-wide hidden slices
-//     (16 KiB of head rows + 16 KiB of hidden rows per stage) by 16-byte
-//     global->LDS DMA; 16-byte chunks are XOR-swizzled per row so that the
-//     MFMA operand reads are free of bank conflicts.
-//   - 8 waves: wave w covers head rows (w % 4)*64 .. +63 and positions
-//     (w / 4)*128 .. +127 of the tile, 2 x 4 blocks of 32 x 32.  In the
-//     transposed orientation a lane holds 16 logits of one position per
+//   - Operands stream through a 2-stage LDS ring of 64-wide hidden slices
+//     (32 KiB of head rows + 32 KiB of hidden rows per stage, one 128-byte
+//     line per row) by 16-byte global->LDS DMA; 16-byte chunks are
+//     XOR-swizzled per row so that the MFMA operand reads are free of bank
+//     conflicts.
+//   - 16 waves, four per SIMD: wave w covers head rows (w % 4)*64 .. +63 and
+//     positions (w / 4)*64 .. +63 of the tile, 2 x 2 blocks of 32 x 32.  In
+//     the transposed orientation a lane holds 16 logits of one position per
 //     block, so the reduction over the vocabulary is mostly in-lane.
 //   - Tiles are numbered with the position tile fastest and dealt to the
 //     XCDs in contiguous ranges, so the position tiles that share a slice of
 //     the head run together on one XCD and read it from its L2.
+//   Measured at 64 x 16 positions, H = 4096, V = 131072 (median of 5 x 10
+//   launches): this configuration 932 us; 32-wide slices in a 4-stage ring,
+//   8 waves of 64 x 128: 1154 us; 4 waves of 128 x 128: 1246 us.  Without
+//   the in-loop DMA (a timing-only copy) the same tiles take 755-792 us, the
+//   rate of the MFMA work and barriers alone at this chip's power limit.
 // lmhead_merge: one workgroup per position merges the tiles' partials in
 //   tile order (deterministic) into one partial, which the commit's
 //   per-sequence decision kernel then takes as a single vocabulary part.
@@ -34,28 +40,39 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256;          // positions per tile
-constexpr int kTN = 256;          // head rows (token ids) per tile
-constexpr int kTK = 32;           // hidden units per pipeline stage
-constexpr int kStages = 4;
-constexpr int kThreads = 512;
-constexpr int kRowBytes = kTK * 2;                     // 64 bytes of one row per stage
-constexpr int kStageBytes = (kTN + kTM) * kRowBytes;   // 32 KiB
+constexpr int kTM = 256;
+constexpr int kTN = 256;
+constexpr int kTK = 64;           // hidden units per pipeline stage: 128-byte rows
+constexpr int kStages = 2;        // double buffer: 2 x 64 KiB of LDS
+constexpr int kWaves = 16;        // 4 per SIMD; wave tile 64 head rows x 64 positions
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = kTK * 2;
+constexpr int kStageBytes = (kTN + kTM) * kRowBytes;
+constexpr int kRPB = 256 / kRowBytes;          // rows per 256 bytes
+constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
+constexpr int kRPI = 1024 / kRowBytes;         // rows per 1 KiB DMA instruction
+constexpr int kInstr = kTN * kRowBytes / 1024; // DMA instructions per operand per stage
+constexpr int kIPW = kInstr / kWaves;          // per wave and operand
+constexpr int WN = 4, WM = kWaves / 4;
+constexpr int TNW = kTN / WN, TMW = kTM / WM;
+constexpr int NI = TNW / 32, NJ = TMW / 32;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kNoIndex = 0x7fffffff;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // 16-byte global->LDS DMA of one wave: lane i's 16 bytes from base + voff
 // land at LDS byte address lds_base + 16*i.  Written in asm (no outputs) so
 // that the compiler neither waits for it nor orders LDS reads behind it;
 // completion is checked with explicit vmcnt waits before the barrier that
 // publishes a stage.  It sets M0 itself, which is safe while the compiler
 // keeps nothing of its own in M0 (checked on the generated assembly by
-// tests/test_kernel_asm.py).
+// tests/test_kernel_asm.py).  The head slice is re-read by the other
+// position tiles and the hidden rows by every head tile, through L2: no
+// non-temporal hint (sc1 only: 932 us against 951 us with nt at the batched
+// step's shape).
 __device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1 nt\n\ts_nop 1"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1\n\ts_nop 1"
                :
                : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
@@ -68,21 +85,23 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Wait until at most n of this wave's DMA instructions are outstanding.
-__device__ inline void wait_dma(int n) {
-  if (n >= 8) __builtin_amdgcn_s_waitcnt(0xF70 | 8);
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0xF70 | 4);
-  else __builtin_amdgcn_s_waitcnt(0xF70);
+template <int PER>
+__device__ inline void wait_dma(int ahead) {
+  // at most PER * ahead of this wave's DMA instructions outstanding (ahead <= 2)
+  if (ahead >= 2) {
+    if constexpr (2 * PER >= 16) __builtin_amdgcn_s_waitcnt((0xF70 | ((2 * PER) & 15)) | (((2 * PER) >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PER));
+  } else if (ahead == 1) {
+    if constexpr (PER >= 16) __builtin_amdgcn_s_waitcnt((0xF70 | (PER & 15)) | ((PER >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0xF70 | PER);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0xF70);
+  }
 }
-// chunk swizzle of a 64-byte row: logical 16-byte chunk c of row r sits at
-// c ^ ((r >> 2) & 3), so 16 consecutive rows read at one logical chunk hit
-// 16 distinct 16-byte bank groups
-__device__ inline int swz(int r) { return (r >> 2) & 3; }
-
-// merge (m, z, idx) partials: larger max, then lower index; z rescaled
+__device__ inline int swz(int r) { return (r / kRPB) % kCPR; }
 __device__ inline void merge_part(float &m, float &z, int &idx, float om, float oz, int oi) {
   const float M = fmaxf(m, om);
-  if (M == kNegInf) return;                 // both empty
+  if (M == kNegInf) return;
   const float za = (m == kNegInf) ? 0.f : z * fast_exp2((m - M) * kLog2e);
   const float zb = (om == kNegInf) ? 0.f : oz * fast_exp2((om - M) * kLog2e);
   int I = kNoIndex;
@@ -93,156 +112,174 @@ __device__ inline void merge_part(float &m, float &z, int &idx, float om, float 
   idx = I;
 }
 
+// Positions still to score, in order: rows[0 .. *count) lists every i with
+// masked[i] != 0 (one workgroup, a ballot scan per 1024 positions).
+__global__ __launch_bounds__(1024) void lmhead_compact(const uint8_t *__restrict__ masked, int M,
+                                                      int32_t *__restrict__ rows,
+                                                      int32_t *__restrict__ count) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  int base = 0;
+  for (int c0 = 0; c0 < M; c0 += 1024) {
+    const int i = c0 + tid;
+    const bool f = i < M && masked[i] != 0;
+    const unsigned long long bal = __ballot(f);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      off += k < w ? wsum[k] : 0;
+      tot += wsum[k];
+    }
+    if (f) rows[base + off + pre] = i;
+    __syncthreads();
+    base += tot;
+  }
+  if (tid == 0) *count = base;
+}
+
+// rows / count: the compacted positions (NULL: all M positions in order).
+// Tile tm covers compacted positions tm*256 .. +255; tiles past the count
+// return at once.
 __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     const bf16 *__restrict__ hidden, const bf16 *__restrict__ whead, int M, int V, int H,
-    int m_tiles, int n_tiles, Part *__restrict__ parts) {
+    int m_tiles, int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
+    Part *__restrict__ parts) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
-  const int wn = w & 3, wm = w >> 2;
-
-  // XCD-aware tile number: workgroup b runs on XCD b % 8; XCD x takes the
-  // contiguous tile range [x*q + min(x, r), ...) of its q or q+1 tiles
+  const int wn = w % WN, wm = w / WN;
   const int nwg = m_tiles * n_tiles;
   const int b = blockIdx.x, x = b & 7, k = b >> 3;
   const int q = nwg >> 3, r8 = nwg & 7;
   const int t = x * q + (x < r8 ? x : r8) + k;
   const int tn = t / m_tiles, tm = t - tn * m_tiles;
   const int n0 = tn * kTN, m0 = tm * kTM;
-
-  // DMA plan: per stage, 16 KiB of head rows (16 wave-instructions of 1 KiB)
-  // then 16 KiB of hidden rows; wave w issues head instructions w and w + 8
-  // and hidden instructions w and w + 8.  Instruction i fills rows
-  // 16i .. 16i+15: lane l writes physical chunk l % 4 of row 16i + l / 4,
-  // which holds logical chunk (l % 4) ^ swz(row).  Rows past V or M re-read
-  // the last valid row (finite data; those logits are masked or dropped).
-  uint32_t voff_w[2], voff_h[2];
+  const int Mc = count ? *count : M;
+  if (m0 >= Mc) return;
+  uint32_t voff_w[kIPW], voff_h[kIPW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = w + 8 * u;
-    const int row = 16 * i + (lane >> 2);
-    const int c = (lane & 3) ^ swz(row);
+  for (int u = 0; u < kIPW; ++u) {
+    const int i = w + kWaves * u;
+    const int row = kRPI * i + lane / kCPR;
+    const int c = (lane % kCPR) ^ swz(row);
     const int rw = min(n0 + row, V - 1) - n0;
-    const int rh = min(m0 + row, M - 1) - m0;
+    const int cm = min(m0 + row, Mc - 1);
+    const int rh = rows ? rows[cm] : cm;        // hidden row of this position
     voff_w[u] = uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
     voff_h[u] = uint32_t(rh) * uint32_t(H) * 2u + uint32_t(c) * 16u;
   }
   const bf16 *wbase = whead + int64_t(n0) * H;
-  const bf16 *hbase = hidden + int64_t(m0) * H;
+  const bf16 *hbase = hidden;
   const uint32_t lds0 = lds_addr(ring);
   const int nk = H / kTK;
-
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + uint32_t((kt % kStages) * kStageBytes);
     const bf16 *wb = wbase + kt * kTK, *hb = hbase + kt * kTK;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t i = uint32_t(w + 8 * u);
+    for (int u = 0; u < kIPW; ++u) {
+      const uint32_t i = uint32_t(w + kWaves * u);
       dma16(wb, voff_w[u], __builtin_amdgcn_readfirstlane(st + i * 1024u));
       dma16(hb, voff_h[u], __builtin_amdgcn_readfirstlane(st + uint32_t(kTN * kRowBytes) + i * 1024u));
     }
   };
-
-  f32x16 acc[2][4];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
-
   for (int kt = 0; kt < nk; ++kt) {
-    // stages issued so far: up to min(kt + kStages - 2, nk - 1); this wave
-    // has 4 DMA instructions per stage, and stage kt must have landed
     const int ahead = min(kStages - 2, nk - 1 - kt);
-    wait_dma(4 * ahead);
-    lds_barrier();                 // stage kt visible; stage kt-1 free for reuse
+    wait_dma<2 * kIPW>(ahead);     // this wave's part of stage kt has landed
+    lds_barrier();                 // all of stage kt visible; stage kt-1 free for reuse
     if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
     const unsigned char *st = ring + (kt % kStages) * kStageBytes;
     const unsigned char *wl = st, *hl = st + kTN * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < kTK / 16; ++ks) {
       const int c = ks * 2 + lh;
-      bf16x8 a[2], bb[4];
+      bf16x8 a[NI], bb[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wn * 64 + i * 32 + lq;
+      for (int i = 0; i < NI; ++i) {
+        const int row = wn * TNW + i * 32 + lq;
         a[i] = *reinterpret_cast<const bf16x8 *>(wl + row * kRowBytes + ((c ^ swz(row)) * 16));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wm * 128 + j * 32 + lq;
+      for (int j = 0; j < NJ; ++j) {
+        const int row = wm * TMW + j * 32 + lq;
         bb[j] = *reinterpret_cast<const bf16x8 *>(hl + row * kRowBytes + ((c ^ swz(row)) * 16));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
   }
-
-  // ---- epilogue: per position, (max, lowest argmax, sum exp) over the tile
-  // acc[i][j] element e of lane (lq, lh): head row n0 + wn*64 + i*32 +
-  // (e >> 2)*8 + lh*4 + (e & 3), position m0 + wm*128 + j*32 + lq
-  float pm[4], pz[4];
-  int pi[4];
+  float pm[NJ], pz[NJ];
+  int pi[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     float mx = kNegInf;
     int id = kNoIndex;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int n = n0 + wn * 64 + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        const int n = n0 + wn * TNW + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
         const float v = n < V ? acc[i][j][e] : kNegInf;
         acc[i][j][e] = v;
-        if (v > mx) { mx = v; id = n; }     // n increases along (i, e): first max wins
+        if (v > mx) { mx = v; id = n; }
       }
     float z = 0.f;
     if (mx != kNegInf) {
       const float mc = mx * kLog2e;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) z += fast_exp2(__builtin_fmaf(acc[i][j][e], kLog2e, -mc));
     }
-    // the other lane half holds the other head rows of the same position
     merge_part(mx, z, id, __shfl_xor(mx, 32), __shfl_xor(z, 32), __shfl_xor(id, 32));
     pm[j] = mx; pz[j] = z; pi[j] = id;
   }
-  lds_barrier();                   // every wave is done with the ring
-  float *red_m = reinterpret_cast<float *>(ring);                 // [4][kTM]
-  float *red_z = red_m + 4 * kTM;
-  int *red_i = reinterpret_cast<int *>(red_z + 4 * kTM);
+  lds_barrier();
+  float *red_m = reinterpret_cast<float *>(ring);
+  float *red_z = red_m + WN * kTM;
+  int *red_i = reinterpret_cast<int *>(red_z + WN * kTM);
   if (lh == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = wm * 128 + j * 32 + lq;
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wm * TMW + j * 32 + lq;
       red_m[wn * kTM + p] = pm[j];
       red_z[wn * kTM + p] = pz[j];
       red_i[wn * kTM + p] = pi[j];
     }
   }
   lds_barrier();
-  if (tid < kTM && m0 + tid < M) {
-    float mx = red_m[tid], z = red_z[tid];
-    int id = red_i[tid];
+  for (int p = tid; p < kTM; p += kThreads) {
+    if (m0 + p >= Mc) break;
+    float mx = red_m[p], z = red_z[p];
+    int id = red_i[p];
 #pragma unroll
-    for (int g = 1; g < 4; ++g) merge_part(mx, z, id, red_m[g * kTM + tid], red_z[g * kTM + tid], red_i[g * kTM + tid]);
+    for (int g = 1; g < WN; ++g) merge_part(mx, z, id, red_m[g * kTM + p], red_z[g * kTM + p], red_i[g * kTM + p]);
     Part pt;
     pt.m = mx; pt.z = z; pt.idx = id; pt.pad = 0;
-    parts[int64_t(m0 + tid) * n_tiles + tn] = pt;
+    parts[int64_t(m0 + p) * n_tiles + tn] = pt;
   }
 }
 
 // One workgroup per position: the n_tiles partials, merged in tile order.
 __global__ __launch_bounds__(256) void lmhead_merge(const Part *__restrict__ parts, int n_tiles,
+                                                   const int32_t *__restrict__ rows,
+                                                   const int32_t *__restrict__ count,
                                                    Part *__restrict__ merged,
                                                    int32_t *__restrict__ n_masked_left) {
   const int row = blockIdx.x, tid = threadIdx.x;
   if (row == 0 && tid == 0 && n_masked_left) *n_masked_left = 0;
+  if (count && row >= *count) return;
   float m = kNegInf, z = 0.f;
   int idx = kNoIndex;
   for (int t = tid; t < n_tiles; t += 256) {
@@ -262,7 +299,7 @@ __global__ __launch_bounds__(256) void lmhead_merge(const Part *__restrict__ par
     for (int g = 1; g < 4; ++g) merge_part(M, Z, I, sm[g], sz[g], si[g]);
     Part p;
     p.m = M; p.z = Z; p.idx = I; p.pad = 0;
-    merged[row] = p;
+    merged[rows ? rows[row] : row] = p;
   }
 }
 
@@ -279,17 +316,26 @@ int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream) {
   const int M = a->B * a->S;
   const int m_tiles = (M + kTM - 1) / kTM;
   const int n_tiles = (a->V + kTN - 1) / kTN;
-  Part *parts = reinterpret_cast<Part *>(ws);
-  Part *merged = reinterpret_cast<Part *>(static_cast<char *>(ws) + align256(lmhead_parts_bytes(a)));
+  char *w = static_cast<char *>(ws);
+  Part *parts = reinterpret_cast<Part *>(w);
+  w += align256(lmhead_parts_bytes(a));
+  Part *merged = reinterpret_cast<Part *>(w);
+  w += align256(size_t(M) * sizeof(Part));
+  int32_t *rows = nullptr, *count = nullptr;
+  if (a->masked_in) {
+    rows = reinterpret_cast<int32_t *>(w);
+    count = rows + M;
+    hipLaunchKernelGGL(lmhead_compact, dim3(1), dim3(1024), 0, st, a->masked_in, M, rows, count);
+  }
   hipLaunchKernelGGL(lmhead_tiles, dim3(unsigned(m_tiles * n_tiles)), dim3(kThreads), 0, st,
                      static_cast<const bf16 *>(a->hidden), static_cast<const bf16 *>(a->w_head), M,
-                     a->V, a->H, m_tiles, n_tiles, parts);
-  hipLaunchKernelGGL(lmhead_merge, dim3(unsigned(M)), dim3(256), 0, st, parts, n_tiles, merged,
-                     a->n_masked_left);
+                     a->V, a->H, m_tiles, n_tiles, rows, count, parts);
+  hipLaunchKernelGGL(lmhead_merge, dim3(unsigned(M)), dim3(256), 0, st, parts, n_tiles, rows, count,
+                     merged, a->n_masked_left);
   if (hipGetLastError() != hipSuccess) return TD_ERR_HIP;
   return launch_commit_finalize(merged, 1, a->B, a->S, a->gamma, a->masked_in, a->commit, a->token,
                                 a->maxprob, a->n_commit, a->masked_out, a->tokens,
-                                a->n_masked_left, stream);
+                                a->n_masked_left, stream, nullptr, a->masked_in != nullptr);
 }
 
 }  // namespace td

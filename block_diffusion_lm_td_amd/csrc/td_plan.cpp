@@ -103,10 +103,11 @@ int validate_lmhead(const td_lmhead_args *a, bool check_ptrs) {
   if (a->dtype != TD_F32 && a->dtype != TD_BF16) return TD_ERR_INVALID;
   if (!finite_f(a->gamma)) return TD_ERR_INVALID;
   if (a->dtype != TD_BF16) return TD_ERR_UNSUPPORTED;
-  if (a->H % 32 != 0 || a->H > 65536 || a->V > (1 << 30)) return TD_ERR_UNSUPPORTED;
+  if (a->H % 64 != 0 || a->H > 65536 || a->V > (1 << 30)) return TD_ERR_UNSUPPORTED;
   const int64_t M = int64_t(a->B) * a->S;
   const int64_t m_tiles = (M + 255) / 256, n_tiles = (int64_t(a->V) + 255) / 256;
   if (M > (1 << 24) || m_tiles * n_tiles > (int64_t(1) << 31) - 1) return TD_ERR_UNSUPPORTED;
+  if (M * a->H * 2 >= (int64_t(1) << 32)) return TD_ERR_UNSUPPORTED;   // 32-bit row offsets
   if (check_ptrs) {
     if (!a->hidden || !a->w_head || !a->commit || !a->token) return TD_ERR_INVALID;
     if (!aligned16(a->hidden) || !aligned16(a->w_head)) return TD_ERR_INVALID;

@@ -173,11 +173,15 @@ typedef struct {
  * commit of td_commit_args over those logits (same outputs, same rules:
  * token = lowest argmax, maxprob = 1 / sum_j exp(logits - max), threshold
  * p >= gamma on the eligible positions, force-one).
+ * Only eligible positions are scored: with masked_in given, the positions
+ * whose masked_in is 0 (already committed) are left out of the product, and
+ * their token is -1 and maxprob 0.  In a block's step loop the work so
+ * shrinks with the number of positions still masked.
  */
 typedef struct {
   int32_t B;               /* >= 1                                             */
   int32_t S;               /* 1 .. 64                                          */
-  int32_t H;               /* hidden size: a multiple of 32, 32 .. 65536       */
+  int32_t H;               /* hidden size: a multiple of 64, 64 .. 65536       */
   int32_t V;               /* vocabulary size, 1 .. 2^30                       */
   td_dtype dtype;          /* TD_BF16 (TD_ERR_UNSUPPORTED otherwise)           */
   float gamma;             /* confidence threshold, finite                     */
@@ -185,8 +189,9 @@ typedef struct {
   const void *w_head;      /* [V, H] LM-head weight, row j = token j            */
   const uint8_t *masked_in;/* [B, S] 1 = still [MASK] (eligible); NULL = all   */
   uint8_t *commit;         /* out [B, S]                                       */
-  int32_t *token;          /* out [B, S]  argmax id at EVERY position          */
-  float *maxprob;          /* out [B, S] or NULL                               */
+  int32_t *token;          /* out [B, S]  argmax id at every eligible position,
+                              -1 at the others                                 */
+  float *maxprob;          /* out [B, S] or NULL (0 at ineligible positions)   */
   int32_t *n_commit;       /* out [B] or NULL                                  */
   uint8_t *masked_out;     /* out [B, S] or NULL; may alias masked_in          */
   int32_t *tokens;         /* in/out [B, S] or NULL: ids written where committed */
@@ -242,9 +247,10 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
                        void *ws, size_t ws_bytes, td_stream_t stream);
 
 /* Fused LM head + commit (see td_lmhead_args).  hidden and w_head must be
- * 16-byte aligned.  The workspace (td_lmhead_commit_workspace_bytes) holds
- * 16 bytes per (position, 256-token slice of the vocabulary).  Returns a
- * td_status. */
+ * 16-byte aligned, and B*S*H*2 below 2^32.  The workspace
+ * (td_lmhead_commit_workspace_bytes) holds 16 bytes per (position, 256-token
+ * slice of the vocabulary), 16 per position and the list of eligible
+ * positions.  Returns a td_status. */
 int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
 
 /* Context-cache append (see td_append_args).  Needs no workspace.  Every

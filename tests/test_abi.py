@@ -208,7 +208,8 @@ def lmhead(**kw):
 @pytest.mark.parametrize("kw,rc", [
     (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(S=65), INVALID), (dict(V=0), INVALID),
     (dict(H=0), INVALID), (dict(dtype=7), INVALID), (dict(gamma=float("inf")), INVALID),
-    (dict(dtype=_td.TD_F32), UNSUPPORTED), (dict(H=100), UNSUPPORTED), (dict(H=65568), UNSUPPORTED),
+    (dict(dtype=_td.TD_F32), UNSUPPORTED), (dict(H=100), UNSUPPORTED), (dict(H=96), UNSUPPORTED),
+    (dict(H=65600), UNSUPPORTED), (dict(B=4096, H=65536), UNSUPPORTED),
     (dict(hidden=None), INVALID), (dict(w_head=None), INVALID), (dict(commit=None), INVALID),
     (dict(token=None), INVALID), (dict(hidden=1 * GB + 2), INVALID), (dict(w_head=2 * GB + 8), INVALID),
 ])
@@ -218,12 +219,13 @@ def test_lmhead_validation(L, kw, rc):
 
 
 def test_lmhead_workspace_bytes(L):
-    """16 bytes per (position, 256-token slice), then 16 per position."""
+    """16 bytes per (position, 256-token slice), 16 per position, then the
+    eligible-position list and its count (each piece 256-byte aligned)."""
     a = lmhead()
     parts = 64 * 16 * 512 * 16
-    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(a)) == parts + 64 * 16 * 16
+    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(a)) == parts + 1024 * 16 + 1025 * 4
     b = lmhead(V=257, B=1, S=3)
-    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(b)) == 256 + 3 * 16
+    assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(b)) == 256 + 256 + 4 * 4
     assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(lmhead(H=100))) == 0
     need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
     assert L.td_lmhead_commit(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE

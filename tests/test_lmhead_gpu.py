@@ -7,8 +7,8 @@ exactly representable in fp32, so the kernel's logits equal the oracle's
 whatever the summation order, and the comparison is the commit's own (tokens
 bit-exact; commit masks bit-exact except positions whose oracle maxprob lies
 within 1e-4 of gamma, excluded and counted).  Shapes span several 256-row and
-256-token tiles with ragged tails, hidden sizes below and above the 4-stage
-pipeline depth, and the full batched step (sampled sequences).  The realistic
+256-token tiles with ragged tails, hidden sizes of one to 64 pipeline
+stages, and the full batched step (sampled sequences).  The realistic
 (non-grid) inputs are checked with a band derived from fp32 accumulation:
 see test_lmhead_realistic_sampled."""
 import numpy as np
@@ -62,6 +62,13 @@ def _case(w, seed, gamma, frac=1.0, seqs=None, label=""):
     g = _run(d, masked, gamma, tokens_in)
     seqs = list(range(B)) if seqs is None else list(seqs)
     ref = _ref(d, masked, gamma, seqs)
+    # positions already committed are not scored: token -1, maxprob 0; the
+    # oracle's values stand in for them in the commit comparison
+    idle = ~masked.astype(bool)
+    assert (g["token"][idle] == -1).all() and (g["maxprob"][idle] == 0).all(), "unscored positions"
+    ri = idle[seqs]
+    g["token"][seqs] = np.where(ri, ref["token"], g["token"][seqs])
+    g["maxprob"][seqs] = np.where(ri, ref["maxprob"], g["maxprob"][seqs])
     return compare_commit(g, ref, masked, gamma, tokens_in, label or w.name, seqs)
 
 
@@ -71,9 +78,9 @@ def test_lmhead_exact_b4(gamma, frac):
 
 
 @pytest.mark.parametrize("B,S,H,V", [
-    (20, 16, 96, 300),       # 320 rows: two position tiles, ragged; 3 stages < pipeline depth
-    (1, 16, 32, 256),        # one stage, exactly one token tile
-    (3, 64, 160, 1),         # a one-token vocabulary
+    (20, 16, 192, 300),      # 320 rows: two position tiles, ragged; 3 stages
+    (1, 16, 64, 256),        # one stage, exactly one token tile
+    (3, 64, 128, 1),         # a one-token vocabulary
     (2, 1, 64, 7),           # S = 1, tiny vocabulary
     (9, 32, 512, 2049),      # 288 rows, 9 token tiles (one token in the last)
     (16, 16, 4096, 1000),    # the widest exact hidden size
@@ -81,6 +88,15 @@ def test_lmhead_exact_b4(gamma, frac):
 def test_lmhead_exact_shapes(B, S, H, V):
     w = LW["lmhead_exact_b4_h256_v5000"].with_(B=B, S=S, H=H, V=V)
     _case(w, 62 + B + H, 0.8, 0.75, label=f"exact B{B} S{S} H{H} V{V}")
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.02, 0.3])
+def test_lmhead_exact_few_positions_left(frac):
+    """Late steps of a block: few positions still masked (none, one or two
+    per sequence, about a third), so only a part of the first position tile
+    or none of it is scored."""
+    w = LW["lmhead_exact_b4_h256_v5000"].with_(B=24)
+    _case(w, 66, 0.8, max(frac, 1e-9), label=f"exact few left frac={frac}")
 
 
 def test_lmhead_exact_full_step_sampled():

@@ -93,11 +93,7 @@ def cpu_baseline(w, a, c, el, budget_s):
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
     f64 = synth.bf16_bits_to_f64
     t_attn = t_commit = 0.0
     keys = 0
@@ -125,6 +121,15 @@ def cpu_baseline(w, a, c, el, budget_s):
                       f"batch by context keys (attention) and sequence count (commit)",
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model()}
+
+
+def blas_threads():
+    """Threads the oracle's numpy BLAS calls use on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
 
 def cpu_model():
@@ -393,6 +398,148 @@ def cache_append_bench(args, L):
     print(json.dumps(res), flush=True)
 
 
+LMHEAD_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_lmhead.hip")
+LMHEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic_lmhead_bf16_b64_h4096_v131072.json")
+
+
+def lmhead_bench(args, L):
+    """td_lmhead_commit on the batched step's 64 x 16 positions with a 4096 x
+    131072 bf16 head: one JSON line.  value = fused steps/s with every
+    position still masked (a block's first step); the same call with 50 / 25 /
+    10 % of the positions still masked (later steps) is reported beside it,
+    and so is the unfused route timed in the same run (the library GEMM of
+    torch writing bf16 logits, then td_commit) for reference."""
+    import numpy as np
+    import torch
+    import block_diffusion_lm_td_amd as td
+    from block_diffusion_lm_td_amd import _td
+    import synth
+
+    w = synth.LMHEAD_WORKLOADS["lmhead_bf16_b64_h4096_v131072"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[lmhead] generating {w.name}")
+    d = synth.make_lmhead_inputs(w, args.seed)
+    B, S, H, V = w.B, w.S, w.H, w.V
+    hid = torch.from_numpy(d["hidden"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wh = torch.from_numpy(d["w_head"].view(np.int16)).view(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    o = dict(commit=torch.empty((B, S), dtype=torch.uint8, device=dev),
+             token=torch.empty((B, S), dtype=torch.int32, device=dev),
+             maxprob=torch.empty((B, S), dtype=torch.float32, device=dev),
+             n_commit=torch.empty((B,), dtype=torch.int32, device=dev),
+             masked_out=torch.empty((B, S), dtype=torch.uint8, device=dev),
+             n_left=torch.empty((1,), dtype=torch.int32, device=dev))
+    rng = np.random.default_rng([args.seed, 11])
+    flops_per_row = 2.0 * H * V
+
+    def timed(call, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            ev[2 * i].record(stream)
+            call()
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]))
+
+    rows = {}
+    for frac in [float(x) for x in args.fracs.split(",")]:
+        m = (rng.random((B, S)) < frac).astype(np.uint8) if frac < 1.0 else np.ones((B, S), np.uint8)
+        mi = torch.from_numpy(m).to(dev)
+        a = td.lmhead_args(hid, wh, o["commit"], o["token"], w.gamma, mi, o["maxprob"], o["n_commit"],
+                           o["masked_out"], None, o["n_left"])
+        need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def call():
+            r = L.td_lmhead_commit(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), need, sp)
+            if r != 0:
+                raise RuntimeError(_td.status_str(r))
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            call()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        launch_ms = timed(call, args.steps)
+        n_rows = int(m.sum())
+        rows[frac] = dict(eligible_positions=n_rows, ms_per_step=round(ms, 5),
+                          avg_launch_us=round(launch_ms * 1e3, 2),
+                          tflops=round(n_rows * flops_per_row / (launch_ms * 1e-3) / 1e12, 1),
+                          committed=int(o["n_commit"].sum().item()))
+        log(f"[lmhead] eligible {n_rows}: {ms * 1e3:.1f} us/step")
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    # the unfused route, for reference: bf16 logits from the library GEMM, then td_commit
+    logits = torch.empty((B, S, V), dtype=torch.bfloat16, device=dev)
+    c = td.commit_args(logits, o["commit"], o["token"], w.gamma, None, o["maxprob"])
+    cneed = max(L.td_commit_workspace_bytes(ctypes.byref(c)), 256)
+    cws = torch.empty(cneed, dtype=torch.uint8, device=dev)
+    wht = wh.t()
+
+    def unfused():
+        torch.matmul(hid.view(B * S, H), wht, out=logits.view(B * S, V))
+        r = L.td_commit(ctypes.byref(c), ctypes.c_void_p(cws.data_ptr()), cneed, sp)
+        if r != 0:
+            raise RuntimeError(_td.status_str(r))
+    for _ in range(args.warmup):
+        unfused()
+    unfused_ms = timed(unfused, args.steps)
+    del logits
+
+    full = rows[max(rows)]
+    achieved = full["tflops"]
+    res = {
+        "metric": "fused LM head + commit: steps/s (64 x 16 positions, H 4096, V 131072) and % of "
+                  "bf16 MFMA roofline, 1 GPU",
+        "value": round(1e3 / full["ms_per_step"], 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": full["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "S": S, "H": H, "V": V, "gamma": w.gamma,
+                   "hidden_size": "assumed (not on the pages)"},
+        "roofline": {"bound": "mfma", "kernel": "td_lmhead_commit (lmhead_tiles + merge + finalize)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, LMHEAD_SRC, LMHEAD_TRAFFIC_FILE),
+                     "algorithmic_flops": B * S * flops_per_row,
+                     "avg_launch_us": full["avg_launch_us"]},
+        "by_eligible_fraction": {str(k): v for k, v in rows.items()},
+        "unfused_reference_us": round(unfused_ms * 1e3, 2),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = synth.bf16_bits_to_f64
+        c0 = time.perf_counter()
+        wf = f64(d["w_head"])
+        n, spent = 0, time.perf_counter() - c0
+        while spent < args.cpu_budget and n < B:
+            c0 = time.perf_counter()
+            oracle.lmhead_commit(f64(d["hidden"][n:n + 1]), wf, None, w.gamma)
+            spent += time.perf_counter() - c0
+            n += 1
+        res["cpu_baseline"] = {"value": round(n / (B * spent), 5), "unit": "steps/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{n} of {B} sequences (all {S} positions over the full "
+                                         f"vocabulary, fp64 numpy), {spent:.1f} s including the "
+                                         f"head's conversion; scaled to the batch by sequence count",
+                               "cpu_model": cpu_model()}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +559,12 @@ def main():
                     help="run --hold-part back-to-back for this many seconds (for sampling board "
                          "power and clocks from outside), print one JSON line and exit")
     ap.add_argument("--hold-part", choices=("step", "attn", "commit"), default="attn")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="time td_lmhead_commit (fused LM head + commit) instead of the step "
+                         "(one JSON line)")
+    ap.add_argument("--fracs", default="1,0.5,0.25,0.1",
+                    help="--lmhead: fractions of positions still masked to time (the first "
+                         "is the headline)")
     ap.add_argument("--append", action="store_true",
                     help="time td_cache_append on the workload's cache instead of the step "
                          "(one JSON line)")
@@ -436,6 +589,9 @@ def main():
         return
     if args.append:
         cache_append_bench(args, L)
+        return
+    if args.lmhead:
+        lmhead_bench(args, L)
         return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

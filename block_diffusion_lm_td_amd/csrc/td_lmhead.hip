@@ -46,6 +46,7 @@ constexpr int kTK = 64;           // hidden units per pipeline stage: 128-byte r
 constexpr int kStages = 2;        // double buffer: 2 x 64 KiB of LDS
 constexpr int kWaves = 16;        // 4 per SIMD; wave tile 64 head rows x 64 positions
 constexpr int kThreads = 64 * kWaves;
+constexpr int kGrid = 256;        // persistent: one workgroup per CU of MI355X
 constexpr int kRowBytes = kTK * 2;
 constexpr int kStageBytes = (kTN + kTM) * kRowBytes;
 constexpr int kRPB = 256 / kRowBytes;          // rows per 256 bytes
@@ -140,134 +141,142 @@ __global__ __launch_bounds__(1024) void lmhead_compact(const uint8_t *__restrict
   if (tid == 0) *count = base;
 }
 
-// rows / count: the compacted positions (NULL: all M positions in order).
-// Tile tm covers compacted positions tm*256 .. +255; tiles past the count
-// return at once.
+// Persistent: one workgroup per CU (kGrid, a multiple of 8) loops over the
+// tiles.  rows / count: the compacted positions (NULL: all M positions in
+// order); only the ceil(count / 256) position tiles that hold positions are
+// visited.  Tiles are numbered with the position tile fastest; XCD x (the
+// workgroups b with b % 8 == x) takes a contiguous range of them, its
+// workgroups in turn, so the position tiles of one head slice run at the
+// same time on one XCD and share the slice through its L2.
 __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     const bf16 *__restrict__ hidden, const bf16 *__restrict__ whead, int M, int V, int H,
-    int m_tiles, int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
+    int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
     Part *__restrict__ parts) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wn = w % WN, wm = w / WN;
-  const int nwg = m_tiles * n_tiles;
-  const int b = blockIdx.x, x = b & 7, k = b >> 3;
-  const int q = nwg >> 3, r8 = nwg & 7;
-  const int t = x * q + (x < r8 ? x : r8) + k;
-  const int tn = t / m_tiles, tm = t - tn * m_tiles;
-  const int n0 = tn * kTN, m0 = tm * kTM;
   const int Mc = count ? *count : M;
-  if (m0 >= Mc) return;
-  uint32_t voff_w[kIPW], voff_h[kIPW];
-#pragma unroll
-  for (int u = 0; u < kIPW; ++u) {
-    const int i = w + kWaves * u;
-    const int row = kRPI * i + lane / kCPR;
-    const int c = (lane % kCPR) ^ swz(row);
-    const int rw = min(n0 + row, V - 1) - n0;
-    const int cm = min(m0 + row, Mc - 1);
-    const int rh = rows ? rows[cm] : cm;        // hidden row of this position
-    voff_w[u] = uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
-    voff_h[u] = uint32_t(rh) * uint32_t(H) * 2u + uint32_t(c) * 16u;
-  }
-  const bf16 *wbase = whead + int64_t(n0) * H;
-  const bf16 *hbase = hidden;
-  const uint32_t lds0 = lds_addr(ring);
-  const int nk = H / kTK;
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + uint32_t((kt % kStages) * kStageBytes);
-    const bf16 *wb = wbase + kt * kTK, *hb = hbase + kt * kTK;
+  const int m_act = (Mc + kTM - 1) / kTM;
+  const int n_act = m_act * n_tiles;
+  const int x = blockIdx.x & 7, px = blockIdx.x >> 3, PX = gridDim.x >> 3;
+  const int q = n_act >> 3, r8 = n_act & 7;
+  const int x_lo = x * q + (x < r8 ? x : r8), x_n = q + (x < r8 ? 1 : 0);
+  for (int j = px; j < x_n; j += PX) {
+    const int t = x_lo + j;
+    const int tn = t / m_act, tm = t - tn * m_act;
+    const int n0 = tn * kTN, m0 = tm * kTM;
+    uint32_t voff_w[kIPW], voff_h[kIPW];
 #pragma unroll
     for (int u = 0; u < kIPW; ++u) {
-      const uint32_t i = uint32_t(w + kWaves * u);
-      dma16(wb, voff_w[u], __builtin_amdgcn_readfirstlane(st + i * 1024u));
-      dma16(hb, voff_h[u], __builtin_amdgcn_readfirstlane(st + uint32_t(kTN * kRowBytes) + i * 1024u));
+      const int i = w + kWaves * u;
+      const int row = kRPI * i + lane / kCPR;
+      const int c = (lane % kCPR) ^ swz(row);
+      const int rw = min(n0 + row, V - 1) - n0;
+      const int cm = min(m0 + row, Mc - 1);
+      const int rh = rows ? rows[cm] : cm;        // hidden row of this position
+      voff_w[u] = uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
+      voff_h[u] = uint32_t(rh) * uint32_t(H) * 2u + uint32_t(c) * 16u;
     }
-  };
-  f32x16 acc[NI][NJ];
+    const bf16 *wbase = whead + int64_t(n0) * H;
+    const bf16 *hbase = hidden;
+    const uint32_t lds0 = lds_addr(ring);
+    const int nk = H / kTK;
+    auto issue = [&](int kt) {
+      const uint32_t st = lds0 + uint32_t((kt % kStages) * kStageBytes);
+      const bf16 *wb = wbase + kt * kTK, *hb = hbase + kt * kTK;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(kStages - 2, nk - 1 - kt);
-    wait_dma<2 * kIPW>(ahead);     // this wave's part of stage kt has landed
-    lds_barrier();                 // all of stage kt visible; stage kt-1 free for reuse
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    const unsigned char *st = ring + (kt % kStages) * kStageBytes;
-    const unsigned char *wl = st, *hl = st + kTN * kRowBytes;
-#pragma unroll
-    for (int ks = 0; ks < kTK / 16; ++ks) {
-      const int c = ks * 2 + lh;
-      bf16x8 a[NI], bb[NJ];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int row = wn * TNW + i * 32 + lq;
-        a[i] = *reinterpret_cast<const bf16x8 *>(wl + row * kRowBytes + ((c ^ swz(row)) * 16));
+      for (int u = 0; u < kIPW; ++u) {
+        const uint32_t i = uint32_t(w + kWaves * u);
+        dma16(wb, voff_w[u], __builtin_amdgcn_readfirstlane(st + i * 1024u));
+        dma16(hb, voff_h[u], __builtin_amdgcn_readfirstlane(st + uint32_t(kTN * kRowBytes) + i * 1024u));
       }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = wm * TMW + j * 32 + lq;
-        bb[j] = *reinterpret_cast<const bf16x8 *>(hl + row * kRowBytes + ((c ^ swz(row)) * 16));
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  float pm[NJ], pz[NJ];
-  int pi[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    float mx = kNegInf;
-    int id = kNoIndex;
+    };
+    f32x16 acc[NI][NJ];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int n = n0 + wn * TNW + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-        const float v = n < V ? acc[i][j][e] : kNegInf;
-        acc[i][j][e] = v;
-        if (v > mx) { mx = v; id = n; }
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+    for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(kStages - 2, nk - 1 - kt);
+      wait_dma<2 * kIPW>(ahead);     // this wave's part of stage kt has landed
+      lds_barrier();                 // all of stage kt visible; stage kt-1 free for reuse
+      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      const unsigned char *st = ring + (kt % kStages) * kStageBytes;
+      const unsigned char *wl = st, *hl = st + kTN * kRowBytes;
+#pragma unroll
+      for (int ks = 0; ks < kTK / 16; ++ks) {
+        const int c = ks * 2 + lh;
+        bf16x8 a[NI], bb[NJ];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int row = wn * TNW + i * 32 + lq;
+          a[i] = *reinterpret_cast<const bf16x8 *>(wl + row * kRowBytes + ((c ^ swz(row)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int row = wm * TMW + j * 32 + lq;
+          bb[j] = *reinterpret_cast<const bf16x8 *>(hl + row * kRowBytes + ((c ^ swz(row)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
-    float z = 0.f;
-    if (mx != kNegInf) {
-      const float mc = mx * kLog2e;
+    }
+    float pm[NJ], pz[NJ];
+    int pi[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float mx = kNegInf;
+      int id = kNoIndex;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) z += fast_exp2(__builtin_fmaf(acc[i][j][e], kLog2e, -mc));
-    }
-    merge_part(mx, z, id, __shfl_xor(mx, 32), __shfl_xor(z, 32), __shfl_xor(id, 32));
-    pm[j] = mx; pz[j] = z; pi[j] = id;
-  }
-  lds_barrier();
-  float *red_m = reinterpret_cast<float *>(ring);
-  float *red_z = red_m + WN * kTM;
-  int *red_i = reinterpret_cast<int *>(red_z + WN * kTM);
-  if (lh == 0) {
+        for (int e = 0; e < 16; ++e) {
+          const int n = n0 + wn * TNW + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+          const float v = n < V ? acc[i][j][e] : kNegInf;
+          acc[i][j][e] = v;
+          if (v > mx) { mx = v; id = n; }
+        }
+      float z = 0.f;
+      if (mx != kNegInf) {
+        const float mc = mx * kLog2e;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int p = wm * TMW + j * 32 + lq;
-      red_m[wn * kTM + p] = pm[j];
-      red_z[wn * kTM + p] = pz[j];
-      red_i[wn * kTM + p] = pi[j];
-    }
-  }
-  lds_barrier();
-  for (int p = tid; p < kTM; p += kThreads) {
-    if (m0 + p >= Mc) break;
-    float mx = red_m[p], z = red_z[p];
-    int id = red_i[p];
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int g = 1; g < WN; ++g) merge_part(mx, z, id, red_m[g * kTM + p], red_z[g * kTM + p], red_i[g * kTM + p]);
-    Part pt;
-    pt.m = mx; pt.z = z; pt.idx = id; pt.pad = 0;
-    parts[int64_t(m0 + p) * n_tiles + tn] = pt;
+          for (int e = 0; e < 16; ++e) z += fast_exp2(__builtin_fmaf(acc[i][j][e], kLog2e, -mc));
+      }
+      merge_part(mx, z, id, __shfl_xor(mx, 32), __shfl_xor(z, 32), __shfl_xor(id, 32));
+      pm[j] = mx; pz[j] = z; pi[j] = id;
+    }
+    lds_barrier();
+    float *red_m = reinterpret_cast<float *>(ring);
+    float *red_z = red_m + WN * kTM;
+    int *red_i = reinterpret_cast<int *>(red_z + WN * kTM);
+    if (lh == 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int p = wm * TMW + j * 32 + lq;
+        red_m[wn * kTM + p] = pm[j];
+        red_z[wn * kTM + p] = pz[j];
+        red_i[wn * kTM + p] = pi[j];
+      }
+    }
+    lds_barrier();
+    for (int p = tid; p < kTM; p += kThreads) {
+      if (m0 + p >= Mc) break;
+      float mx = red_m[p], z = red_z[p];
+      int id = red_i[p];
+#pragma unroll
+      for (int g = 1; g < WN; ++g) merge_part(mx, z, id, red_m[g * kTM + p], red_z[g * kTM + p], red_i[g * kTM + p]);
+      Part pt;
+      pt.m = mx; pt.z = z; pt.idx = id; pt.pad = 0;
+      parts[int64_t(m0 + p) * n_tiles + tn] = pt;
+    }
+    lds_barrier();                   // the next tile's DMA reuses the ring
   }
 }
 
@@ -314,7 +323,6 @@ size_t lmhead_parts_bytes(const td_lmhead_args *a) {
 int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int M = a->B * a->S;
-  const int m_tiles = (M + kTM - 1) / kTM;
   const int n_tiles = (a->V + kTN - 1) / kTN;
   char *w = static_cast<char *>(ws);
   Part *parts = reinterpret_cast<Part *>(w);
@@ -327,9 +335,9 @@ int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream) {
     count = rows + M;
     hipLaunchKernelGGL(lmhead_compact, dim3(1), dim3(1024), 0, st, a->masked_in, M, rows, count);
   }
-  hipLaunchKernelGGL(lmhead_tiles, dim3(unsigned(m_tiles * n_tiles)), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(lmhead_tiles, dim3(kGrid), dim3(kThreads), 0, st,
                      static_cast<const bf16 *>(a->hidden), static_cast<const bf16 *>(a->w_head), M,
-                     a->V, a->H, m_tiles, n_tiles, rows, count, parts);
+                     a->V, a->H, n_tiles, rows, count, parts);
   hipLaunchKernelGGL(lmhead_merge, dim3(unsigned(M)), dim3(256), 0, st, parts, n_tiles, rows, count,
                      merged, a->n_masked_left);
   if (hipGetLastError() != hipSuccess) return TD_ERR_HIP;

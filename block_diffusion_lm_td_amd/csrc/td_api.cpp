@@ -16,6 +16,11 @@ int check_ws(size_t need, void *ws, size_t ws_bytes) {
   return TD_OK;
 }
 
+int attn_launch(const td_attn_args *a, const AttnPlan &p, void *ws, td_stream_t stream,
+                const int32_t *gate) {
+  return p.decode ? launch_attn_decode(a, p, ws, stream, gate) : launch_attn(a, p, ws, stream, gate);
+}
+
 int denoise(const td_attn_args *a, const td_commit_args *c, const int32_t *gate, void *ws,
             size_t ws_bytes, td_stream_t stream) {
   int rc = validate_attn(a, true);
@@ -28,7 +33,7 @@ int denoise(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
   const size_t wa = align256(pa.ws_bytes), wc = align256(pc.ws_bytes);
   rc = check_ws(wa + wc, ws, ws_bytes);
   if (rc != TD_OK) return rc;
-  rc = launch_attn(a, pa, ws, stream, gate);
+  rc = attn_launch(a, pa, ws, stream, gate);
   if (rc != TD_OK) return rc;
   return launch_commit(c, pc, static_cast<char *>(ws) + wa, stream, gate);
 }
@@ -80,7 +85,7 @@ int td_block_attn(const td_attn_args *a, void *ws, size_t ws_bytes, td_stream_t 
   const AttnPlan p = plan_attn(a);
   rc = check_ws(p.ws_bytes, ws, ws_bytes);
   if (rc != TD_OK) return rc;
-  return launch_attn(a, p, ws, stream);
+  return attn_launch(a, p, ws, stream, nullptr);
 }
 
 int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t stream) {

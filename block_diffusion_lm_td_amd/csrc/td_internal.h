@@ -15,6 +15,8 @@ constexpr int kKeyTile = 64;      // keys per LDS tile
 constexpr int kWaves = 8;         // 8 waves x 32 rows; two waves share each SIMD
 constexpr int kWGThreads = 64 * kWaves;
 constexpr int kGridWGs = 256;     // persistent grid: one workgroup per CU of MI355X
+constexpr int kDecodePieceKeys = 128;   // keys per wave-piece of the decode path
+constexpr int kDecodeMaxB = 4096;       // sequences whose piece table fits the decode kernel's LDS
 
 // Partial of the commit's vocabulary pass over one part of a row (16 bytes).
 struct Part {
@@ -27,6 +29,7 @@ struct Part {
 // Launch plan of one td_block_attn call, derived on the host from sizes only.
 struct AttnPlan {
   bool mfma;            // bf16, D == 128: MFMA kernel; otherwise the VALU kernel
+  bool decode;          // bf16, D == 128, M <= 16: the decode kernels (units = pieces)
   int G;                // Hq / Hkv
   int M;                // G * S query rows per (b, kv head)
   int row_groups;       // ceil(M / kRowsPerWG) (MFMA) or ceil(M / 64) (VALU)
@@ -64,6 +67,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // (the commit still clears n_masked_left)
 int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
                 const int32_t *gate = nullptr);
+int launch_attn_decode(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
+                       const int32_t *gate = nullptr);
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
                   const int32_t *gate = nullptr);
 int launch_append(const td_append_args *p, void *stream);

@@ -141,7 +141,18 @@ AttnPlan plan_attn(const td_attn_args *a) {
   p.mfma = (a->dtype == TD_BF16 && a->D == 128);
   float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf(float(a->D));
   p.scale_log2 = scale * 1.4426950408889634f;
-  if (p.mfma) {
+  p.decode = p.mfma && p.M <= 16 && a->B <= kDecodeMaxB;
+  if (p.decode) {
+    // pieces of kDecodePieceKeys keys: sum over sequences of
+    // ceil((L_b + S) / piece) <= (total + B*S) / piece + B, per KV head
+    p.row_groups = 1;
+    p.units = int64_t(a->Hkv) * ((a->total_ctx + int64_t(a->B) * a->S) / kDecodePieceKeys + a->B + 1);
+    size_t o = 0;
+    p.off_prefix = o; o += align256(size_t(a->B + 1) * 8);
+    p.off_ml = o;     o += align256(size_t(p.units) * 16 * 8);
+    p.off_o = o;      o += align256(size_t(p.units) * 16 * 128 * 2);
+    p.ws_bytes = o;
+  } else if (p.mfma) {
     p.row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
     p.units = int64_t(a->B) * a->Hkv * p.row_groups;
     const int forced = grid_override();

@@ -79,6 +79,11 @@ WORKLOADS: dict[str, Workload] = {
         "bf16_b4_ctx64k", B=4, S=16, Hq=32, Hkv=2, D=128, ctx_lo=65536,
         ctx_hi=65536, dtype="bf16", qkv_std=1.0, ctx_std=1.0, V=131072,
         logit_model="peak", logit_std=2.0, margin_hi=12.0, gamma=0.8),
+    # One-token decode (S = 1, the AR / mock-AR modes) on the batched cache.
+    "bf16_b64_ragged1k_8k_s1": Workload(
+        "bf16_b64_ragged1k_8k_s1", B=64, S=1, Hq=32, Hkv=2, D=128, ctx_lo=1024,
+        ctx_hi=8192, dtype="bf16", qkv_std=_INV_SQRT128, ctx_std=_INV_SQRT128,
+        V=131072, logit_model="peak", logit_std=2.0, margin_hi=12.0, gamma=0.8),
     # Whole-block loop: 32 sequences of 2K context; S and gamma are swept.
     "bf16_b32_ctx2k_loop": Workload(
         "bf16_b32_ctx2k_loop", B=32, S=16, Hq=32, Hkv=2, D=128, ctx_lo=2048,

@@ -85,7 +85,7 @@ def test_attn_workspace_bytes(L):
     on the batch shape only, never on the context lengths."""
     slot = 256 * 128 * 2 + 256 * 8
     for B, Lmax, S, Hq in [(64, 8192, 16, 32), (4, 65536, 16, 32), (8, 4096, 16, 32),
-                           (32, 2048, 64, 32), (3, 1000, 1, 32)]:
+                           (32, 2048, 64, 32), (3, 1000, 2, 32)]:
         a = attn(B=B, S=S, Hq=Hq, total_ctx=B * Lmax, max_ctx=Lmax)
         ws = L.td_attn_workspace_bytes(ctypes.byref(a))
         assert 2 * 256 * slot <= ws <= 2 * 256 * slot + 64 * 1024 + B * 64
@@ -93,6 +93,21 @@ def test_attn_workspace_bytes(L):
         assert L.td_attn_workspace_bytes(ctypes.byref(a2)) == ws
     f = attn(dtype=_td.TD_F32, D=64)
     assert L.td_attn_workspace_bytes(ctypes.byref(f)) == 0   # VALU path needs none
+
+
+def test_attn_decode_workspace_bytes(L):
+    """At most 16 query rows per KV head (here S = 1, 16 query heads per KV
+    head) take the decode path: one partial (16 x 128 bf16 O / l + 16 fp32
+    (m, l)) per piece of 128 keys, sized by the bound (total + B*S) / 128 +
+    B + 1 pieces per KV head, plus the per-sequence piece table."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    for B, total, S, Hq, Hkv in [(64, 296372, 1, 32, 2), (3, 1000, 1, 32, 2), (1, 0, 1, 4, 1),
+                                 (7, 5000, 2, 16, 2)]:
+        a = attn(B=B, S=S, Hq=Hq, Hkv=Hkv, total_ctx=total, max_ctx=total)
+        P = Hkv * ((total + B * S) // 128 + B + 1)
+        want = a256((B + 1) * 8) + a256(P * 16 * 8) + a256(P * 16 * 128 * 2)
+        assert L.td_attn_workspace_bytes(ctypes.byref(a)) == want, (B, total, S)
 
 
 @pytest.mark.parametrize("kw,rc", [

@@ -729,7 +729,9 @@ def main():
                    "input_sets": nsets},
         "tokens_per_s": round(committed * steps_per_s, 1),
         "committed_per_step": committed,
-        "roofline": {"bound": "hbm", "kernel": "td_block_attn (attn_bf16_mfma + attn_merge)",
+        "roofline": {"bound": "hbm", "kernel": "td_block_attn (attn_decode + decode_merge)"
+                     if w.dtype == "bf16" and w.D == 128 and w.G * w.S <= 16 and w.B <= 4096
+                     else "td_block_attn (attn_bf16_mfma + attn_merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": attn_bytes, "avg_launch_us": round(attn_ms * 1e3, 2),

@@ -12,4 +12,5 @@ from .td_oracle import (  # noqa: F401
     cache_append,
     lmhead_logits,
     lmhead_commit,
+    mamba_block_scan,
 )

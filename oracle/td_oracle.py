@@ -218,3 +218,43 @@ def cache_append(k_ctx, v_ctx, offsets, k_new, v_new):
         offsets_out[b + 1] = offsets_out[b] + (stop - start) + S
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0), offsets_out
 
+
+# ----------------------------------------------------------------------------
+# Denoiser Mamba-2 layer over the block, its state seeded from the context
+# tower ([chathome] inference paragraph: the denoiser's Mamba-2 layers start
+# from the context tower's state; the layer itself is Mamba-2's selective
+# state-space recurrence with one decay rate per head)
+# ----------------------------------------------------------------------------
+def mamba_block_scan(x, dt, A, Bm, Cm, D, h0):
+    """The state-space core of one Mamba-2 layer over the block's S tokens,
+    started from the context tower's final state.
+
+    x  [B, S, H, P]   per-head inputs          dt [B, S, H]  step sizes (> 0)
+    A  [H]            decay rates (< 0)        D  [H]        skip weights
+    Bm, Cm [B, S, G, N]  input / output projections; head h reads group
+                      h // (H / G)
+    h0 [B, H, P, N]   seed state (the context tower's state after its tokens)
+    For every sequence and head, token by token:
+        h <- exp(dt_t * A) * h + dt_t * x_t (outer) B_t
+        y_t = h C_t + D * x_t
+    Returns (y [B, S, H, P], h_S [B, H, P, N]) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    Bm = np.asarray(Bm, dtype=np.float64)
+    Cm = np.asarray(Cm, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    nb, S, H, P = x.shape
+    G = Bm.shape[2]
+    hs = np.array(h0, dtype=np.float64, copy=True)
+    y = np.zeros((nb, S, H, P))
+    for b in range(nb):
+        for h in range(H):
+            grp = h // (H // G)
+            st = hs[b, h]
+            for t in range(S):
+                st = np.exp(dt[b, t, h] * A[h]) * st + dt[b, t, h] * np.outer(x[b, t, h], Bm[b, t, grp])
+                y[b, t, h] = st @ Cm[b, t, grp] + D[h] * x[b, t, h]
+            hs[b, h] = st
+    return y, hs
+

@@ -9,6 +9,8 @@ HIP path consumes the very same bits on the device.
 from .workloads import (  # noqa: F401
     LMHEAD_WORKLOADS,
     LMHeadWorkload,
+    MAMBA_WORKLOADS,
+    MambaWorkload,
     WORKLOADS,
     Workload,
     bf16_bits_to_f32,
@@ -17,6 +19,7 @@ from .workloads import (  # noqa: F401
     make_attention_inputs,
     make_commit_inputs,
     make_lmhead_inputs,
+    make_mamba_inputs,
     make_eligible,
     loop_step_logits,
     loop_peak_values,

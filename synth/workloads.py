@@ -314,3 +314,46 @@ def make_lmhead_inputs(w: LMHeadWorkload, seed: int) -> dict:
     return dict(hidden=f32_to_bf16_bits(g).reshape(w.B, w.S, w.H),
                 w_head=f32_to_bf16_bits(head), peak=peak, margin=margin, dtype="bf16")
 
+
+# ----------------------------------------------------------------------------
+# Denoiser Mamba-2 layer: the block's SSM inputs and the seed state
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class MambaWorkload:
+    name: str
+    B: int
+    S: int
+    H: int               # SSM heads
+    P: int               # head dim
+    N: int               # state size
+    G: int               # groups of B / C projections
+
+    def with_(self, **kw) -> "MambaWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# The pages give no Mamba-2 dimensions; these follow Mamba-2 layers of that
+# model size (128 heads of 64 with a 128-wide state in 8 groups).
+MAMBA_WORKLOADS: dict[str, MambaWorkload] = {
+    "mamba_b4_s16_h8": MambaWorkload("mamba_b4_s16_h8", B=4, S=16, H=8, P=64, N=128, G=2),
+    "mamba_b64_s16_h128": MambaWorkload("mamba_b64_s16_h128", B=64, S=16, H=128, P=64, N=128, G=8),
+}
+
+
+def make_mamba_inputs(w: MambaWorkload, seed: int) -> dict:
+    """x [B,S,H,P], Bm / Cm [B,S,G,N] as bf16 bits; dt [B,S,H], A [H], D [H]
+    and the seed state h0 [B,H,P,N] in float32.  Ranges follow Mamba-2's
+    usual initialisation: dt log-uniform in [1e-3, 1e-1], A = -exp(U(0,
+    ln 16)), D near 1; x, B, C, h0 standard normal.  Draw order: x, dt, A,
+    B, C, D, h0."""
+    rng = np.random.default_rng([seed, 13])
+    x = _normal(rng, (w.B, w.S, w.H, w.P), 1.0)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (w.B, w.S, w.H))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), w.H))).astype(np.float32)
+    Bm = _normal(rng, (w.B, w.S, w.G, w.N), 1.0)
+    Cm = _normal(rng, (w.B, w.S, w.G, w.N), 1.0)
+    D = rng.uniform(0.5, 1.5, w.H).astype(np.float32)
+    h0 = _normal(rng, (w.B, w.H, w.P, w.N), 1.0)
+    return dict(x=f32_to_bf16_bits(x), dt=dt, A=A, Bm=f32_to_bf16_bits(Bm), Cm=f32_to_bf16_bits(Cm),
+                D=D, h0=h0)
+

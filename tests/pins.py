@@ -659,3 +659,125 @@ LMHEAD_LOGIT_PINS = [pin_lmhead_logits_torch, pin_lmhead_logits_brute]
 LMHEAD_PINS = [pin_lmhead_identity_head, pin_lmhead_shift_invariance, pin_lmhead_vocab_permutation,
                pin_lmhead_eligibility]
 
+
+# ----------------------------------------------------------------------------
+# Mamba-2 block-scan pins ([chathome] inference paragraph: the denoiser's
+# Mamba-2 state is seeded from the context tower)
+# ----------------------------------------------------------------------------
+def _ssm_inputs(seed, B=2, S=5, H=4, P=3, N=6, G=2, A_zero=False, dt_zero=False):
+    rng = np.random.default_rng(seed)
+    return dict(
+        x=rng.standard_normal((B, S, H, P)),
+        dt=np.zeros((B, S, H)) if dt_zero else rng.uniform(0.01, 0.3, (B, S, H)),
+        A=np.zeros(H) if A_zero else -rng.uniform(0.5, 4.0, H),
+        Bm=rng.standard_normal((B, S, G, N)),
+        Cm=rng.standard_normal((B, S, G, N)),
+        D=rng.uniform(0.5, 1.5, H),
+        h0=rng.standard_normal((B, H, P, N)))
+
+
+def _call_ssm(scan, a):
+    return scan(a["x"], a["dt"], a["A"], a["Bm"], a["Cm"], a["D"], a["h0"])
+
+
+def pin_mamba_closed_form(scan):
+    """The block as one sum (the quadratic form of the same recurrence): with
+    c_t = sum_{r<=t} dt_r A,
+      y_t = e^{c_t} h0 C_t + sum_{s<=t} e^{c_t - c_s} dt_s (C_t . B_s) x_s + D x_t
+      h_S = e^{c_S} h0 + sum_s e^{c_S - c_s} dt_s x_s (outer) B_s."""
+    a = _ssm_inputs(61)
+    y, hS = _call_ssm(scan, a)
+    nb, S, H, P = a["x"].shape
+    G = a["Bm"].shape[2]
+    for b in range(nb):
+        for h in range(H):
+            g = h // (H // G)
+            c = np.cumsum(a["dt"][b, :, h] * a["A"][h])
+            for t in range(S):
+                want = np.exp(c[t]) * (a["h0"][b, h] @ a["Cm"][b, t, g]) + a["D"][h] * a["x"][b, t, h]
+                for s_ in range(t + 1):
+                    want = want + (np.exp(c[t] - c[s_]) * a["dt"][b, s_, h]
+                                   * (a["Cm"][b, t, g] @ a["Bm"][b, s_, g]) * a["x"][b, s_, h])
+                _close(y[b, t, h], want, tol=1e-10, what=f"y b={b} h={h} t={t}")
+            wantS = np.exp(c[-1]) * a["h0"][b, h]
+            for s_ in range(S):
+                wantS = wantS + (np.exp(c[-1] - c[s_]) * a["dt"][b, s_, h]
+                                 * np.outer(a["x"][b, s_, h], a["Bm"][b, s_, g]))
+            _close(hS[b, h], wantS, tol=1e-10, what=f"h_S b={b} h={h}")
+
+
+def pin_mamba_zero_step(scan):
+    """dt = 0: the state stays the seed, y_t = h0 C_t + D x_t."""
+    a = _ssm_inputs(62, dt_zero=True)
+    y, hS = _call_ssm(scan, a)
+    H, G = a["x"].shape[2], a["Bm"].shape[2]
+    grp = np.arange(H) // (H // G)
+    want = np.einsum("bhpn,bthn->bthp", a["h0"], a["Cm"][:, :, grp]) + a["D"][None, None, :, None] * a["x"]
+    _close(y, want, tol=1e-12, what="dt = 0")
+    _close(hS, a["h0"], tol=0.0, what="state unchanged")
+
+
+def pin_mamba_no_decay(scan):
+    """A = 0: no decay, the state is the seed plus running sums of
+    dt_s x_s (outer) B_s (cumulative sums along the block)."""
+    a = _ssm_inputs(63, A_zero=True)
+    y, hS = _call_ssm(scan, a)
+    H, G = a["x"].shape[2], a["Bm"].shape[2]
+    grp = np.arange(H) // (H // G)
+    upd = np.einsum("bth,bthp,bthn->bthpn", a["dt"], a["x"], a["Bm"][:, :, grp])
+    states = a["h0"][:, None] + np.cumsum(upd, axis=1)
+    want = np.einsum("bthpn,bthn->bthp", states, a["Cm"][:, :, grp]) + a["D"][None, None, :, None] * a["x"]
+    _close(y, want, tol=1e-10, what="A = 0")
+    _close(hS, states[:, -1], tol=1e-10, what="A = 0 final state")
+
+
+def pin_mamba_state_passing(scan):
+    """Scanning the first 3 tokens, then the last 4 from the state they
+    leave, is scanning all 7 at once: the seed is exactly the state the
+    earlier tokens produce (what seeding from the context tower means)."""
+    a = _ssm_inputs(64, S=7)
+    y, hS = _call_ssm(scan, a)
+    first = {k: (v[:, :3] if k in ("x", "dt", "Bm", "Cm") else v) for k, v in a.items()}
+    y1, h1 = _call_ssm(scan, first)
+    second = {k: (v[:, 3:] if k in ("x", "dt", "Bm", "Cm") else v) for k, v in a.items()}
+    second["h0"] = np.asarray(h1)
+    y2, h2 = _call_ssm(scan, second)
+    _close(np.concatenate([np.asarray(y1), np.asarray(y2)], axis=1), y, tol=1e-10, what="split scan")
+    _close(h2, hS, tol=1e-10, what="split final state")
+
+
+def pin_mamba_brute(scan):
+    """Pure-Python loops on a tiny case (one group, scalars only)."""
+    a = _ssm_inputs(65, B=1, S=3, H=2, P=2, N=2, G=1)
+    y, hS = _call_ssm(scan, a)
+    for h in range(2):
+        st = [[float(a["h0"][0, h, p, n]) for n in range(2)] for p in range(2)]
+        for t in range(3):
+            dec = math.exp(float(a["dt"][0, t, h]) * float(a["A"][h]))
+            for p in range(2):
+                for n in range(2):
+                    st[p][n] = dec * st[p][n] + float(a["dt"][0, t, h]) * float(a["x"][0, t, h, p]) * float(a["Bm"][0, t, 0, n])
+            for p in range(2):
+                yt = sum(st[p][n] * float(a["Cm"][0, t, 0, n]) for n in range(2)) + float(a["D"][h]) * float(a["x"][0, t, h, p])
+                assert abs(y[0, t, h, p] - yt) < 1e-12, (h, t, p)
+        for p in range(2):
+            for n in range(2):
+                assert abs(hS[0, h, p, n] - st[p][n]) < 1e-12
+
+
+def pin_mamba_groups(scan):
+    """Heads read their group's projections: with one group per head and each
+    head's projections copied from its group, the result is unchanged."""
+    a = _ssm_inputs(66, H=6, G=2)
+    y, hS = _call_ssm(scan, a)
+    b = dict(a)
+    grp = np.arange(6) // 3
+    b["Bm"], b["Cm"] = a["Bm"][:, :, grp], a["Cm"][:, :, grp]
+    y2, hS2 = _call_ssm(scan, b)
+    _close(y2, y, tol=1e-12, what="groups vs per-head copies")
+    _close(hS2, hS, tol=1e-12, what="groups vs per-head copies (state)")
+
+
+MAMBA_PINS = [pin_mamba_closed_form, pin_mamba_zero_step, pin_mamba_no_decay, pin_mamba_state_passing,
+              pin_mamba_brute, pin_mamba_groups]
+

@@ -43,3 +43,8 @@ def test_lmhead_logits_pin(pin):
 @pytest.mark.parametrize("pin", pins.LMHEAD_PINS, ids=lambda f: f.__name__)
 def test_lmhead_commit_pin(pin):
     pin(oracle.lmhead_commit)
+
+
+@pytest.mark.parametrize("pin", pins.MAMBA_PINS, ids=lambda f: f.__name__)
+def test_mamba_pin(pin):
+    pin(oracle.mamba_block_scan)

@@ -55,6 +55,14 @@ MUTANTS = [
      "confidence_commit(lmhead_logits(hidden, w_head), None, gamma)"),
     ("lmhead_last_hidden_unit_dropped", "(h.reshape(B * S, H) @ w.T)",
      "(h[..., :-1].reshape(B * S, H - 1) @ w[:, :-1].T)"),
+    ("mamba_decay_after_update", "st = np.exp(dt[b, t, h] * A[h]) * st + dt[b, t, h] * np.outer(x[b, t, h], Bm[b, t, grp])",
+     "st = np.exp(dt[b, t, h] * A[h]) * (st + dt[b, t, h] * np.outer(x[b, t, h], Bm[b, t, grp]))"),
+    ("mamba_input_without_step", "+ dt[b, t, h] * np.outer(x[b, t, h], Bm[b, t, grp])",
+     "+ np.outer(x[b, t, h], Bm[b, t, grp])"),
+    ("mamba_group_modulo", "grp = h // (H // G)", "grp = h % G"),
+    ("mamba_output_from_seed", "y[b, t, h] = st @ Cm[b, t, grp]", "y[b, t, h] = hs[b, h] @ Cm[b, t, grp]"),
+    ("mamba_no_skip", "y[b, t, h] = st @ Cm[b, t, grp] + D[h] * x[b, t, h]", "y[b, t, h] = st @ Cm[b, t, grp]"),
+    ("mamba_b_for_c", "np.outer(x[b, t, h], Bm[b, t, grp])", "np.outer(x[b, t, h], Cm[b, t, grp])"),
     ("append_new_rows_truncated", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b, 1:]]"),
 ]
 
@@ -77,6 +85,7 @@ def _all_pins(mod):
     yield from ((p, mod.cache_append) for p in pins.APPEND_PINS)
     yield from ((p, mod.lmhead_logits) for p in pins.LMHEAD_LOGIT_PINS)
     yield from ((p, mod.lmhead_commit) for p in pins.LMHEAD_PINS)
+    yield from ((p, mod.mamba_block_scan) for p in pins.MAMBA_PINS)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

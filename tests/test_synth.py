@@ -69,3 +69,16 @@ def test_lmhead_inputs_deterministic_and_shaped():
     # the head's spread: sw = logit_std / sqrt(H)
     sw = synth.bf16_bits_to_f64(a["w_head"]).std()
     assert abs(sw - 2.0 / 16.0) < 0.005
+
+
+def test_mamba_inputs_deterministic_and_ranged():
+    w = synth.MAMBA_WORKLOADS["mamba_b4_s16_h8"]
+    a = synth.make_mamba_inputs(w, 3)
+    b = synth.make_mamba_inputs(w, 3)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert a["x"].shape == (4, 16, 8, 64) and a["x"].dtype == np.uint16
+    assert a["Bm"].shape == (4, 16, 2, 128) and a["h0"].shape == (4, 8, 64, 128)
+    assert a["h0"].dtype == np.float32 and a["dt"].dtype == np.float32
+    assert (a["dt"] >= 1e-3 * 0.999).all() and (a["dt"] <= 0.1 * 1.001).all()
+    assert (a["A"] <= -1.0 + 1e-6).all() and (a["A"] >= -16.0 - 1e-4).all()

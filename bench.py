@@ -540,6 +540,119 @@ def lmhead_bench(args, L):
     print(json.dumps(res), flush=True)
 
 
+MAMBA_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_mamba.hip")
+MAMBA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mamba_traffic_mamba_b64_s16_h128.json")
+
+
+def mamba_algorithmic(w):
+    """Bytes one block scan must move: the fp32 seed state, x and y (bf16),
+    Bm and Cm (bf16), dt (fp32) and the per-head A and D."""
+    return (w.B * w.H * w.P * w.N * 4 + 2 * w.B * w.S * w.H * w.P * 2
+            + 2 * w.B * w.S * w.G * w.N * 2 + w.B * w.S * w.H * 4 + 2 * w.H * 4)
+
+
+def mamba_bench(args, L):
+    """td_mamba_block_scan on the batched block: 64 sequences x 128 heads of
+    64 with a 128-wide state (8 groups), S = 16, seeded from fp32 states.
+    One JSON line; rotating input sets keep the 256 MB last-level cache from
+    serving the seed states of the previous launch."""
+    import numpy as np
+    import torch
+    import block_diffusion_lm_td_amd as td
+    from block_diffusion_lm_td_amd import _td
+    import synth
+
+    w = synth.MAMBA_WORKLOADS["mamba_b64_s16_h128"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[mamba] generating {w.name}")
+    d = synth.make_mamba_inputs(w, args.seed)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    alg = mamba_algorithmic(w)
+    nsets = args.sets or max(2, int(np.ceil(1.5e9 / alg)))
+    base = dict(x=bf(d["x"]), dt=f32(d["dt"]), A=f32(d["A"]), Bm=bf(d["Bm"]), Cm=bf(d["Cm"]),
+                D=f32(d["D"]), h0=f32(d["h0"]))
+    structs = []
+    keep = []
+    for i in range(nsets):
+        st = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        y = torch.empty((w.B, w.S, w.H, w.P), dtype=torch.bfloat16, device=dev)
+        keep.append((st, y))
+        structs.append(td.mamba_args(st["x"], st["dt"], st["A"], st["Bm"], st["Cm"], st["D"], st["h0"], y))
+    refs = [ctypes.byref(a) for a in structs]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def run(i):
+        r = L.td_mamba_block_scan(refs[i % nsets], sp)
+        if r != 0:
+            raise RuntimeError(_td.status_str(r))
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        run(i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]))
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    res = {
+        "metric": "Mamba-2 block scans/s (64 x 128 heads, S 16, seeded state) and % of HBM "
+                  "roofline, 1 GPU",
+        "value": round(1e3 / ms, 2), "unit": "scans/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_scan": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "P": w.P, "N": w.N, "G": w.G,
+                   "dims": "assumed (not on the pages)", "sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "td_mamba_block_scan (mamba_block)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, MAMBA_SRC, MAMBA_TRAFFIC_FILE),
+                     "algorithmic_bytes": alg, "avg_launch_us": round(launch_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = synth.bf16_bits_to_f64
+        n, spent = 0, 0.0
+        while spent < args.cpu_budget and n < w.B:
+            c0 = time.perf_counter()
+            oracle.mamba_block_scan(f64(d["x"][n:n + 1]), d["dt"][n:n + 1], d["A"], f64(d["Bm"][n:n + 1]),
+                                    f64(d["Cm"][n:n + 1]), d["D"], d["h0"][n:n + 1])
+            spent += time.perf_counter() - c0
+            n += 1
+        res["cpu_baseline"] = {"value": round(n / (w.B * spent), 4), "unit": "scans/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{n} of {w.B} sequences (all 128 heads, token by token, "
+                                         f"fp64 numpy), {spent:.1f} s; scaled to the batch by "
+                                         f"sequence count", "cpu_model": cpu_model()}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -565,6 +678,8 @@ def main():
     ap.add_argument("--fracs", default="1,0.5,0.25,0.1",
                     help="--lmhead: fractions of positions still masked to time (the first "
                          "is the headline)")
+    ap.add_argument("--mamba", action="store_true",
+                    help="time td_mamba_block_scan instead of the step (one JSON line)")
     ap.add_argument("--append", action="store_true",
                     help="time td_cache_append on the workload's cache instead of the step "
                          "(one JSON line)")
@@ -592,6 +707,9 @@ def main():
         return
     if args.lmhead:
         lmhead_bench(args, L)
+        return
+    if args.mamba:
+        mamba_bench(args, L)
         return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

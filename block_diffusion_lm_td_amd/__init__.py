@@ -9,12 +9,14 @@ from ._td import (  # noqa: F401
     TdAttnArgs,
     TdCommitArgs,
     TdLmheadArgs,
+    TdMambaArgs,
     Workspace,
     append_args,
     attn_args,
     commit_args,
     header_functions,
     lmhead_args,
+    mamba_args,
     lib,
     status_str,
     td_block_attn,
@@ -23,4 +25,5 @@ from ._td import (  # noqa: F401
     td_denoise_step,
     td_denoise_step_if,
     td_lmhead_commit,
+    td_mamba_block_scan,
 )

@@ -50,6 +50,12 @@ class TdLmheadArgs(ctypes.Structure):
                 ("tokens", c_void_p), ("n_masked_left", c_void_p)]
 
 
+class TdMambaArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("H", c_int32), ("P", c_int32), ("N", c_int32),
+                ("G", c_int32), ("x", c_void_p), ("dt", c_void_p), ("A", c_void_p), ("Bm", c_void_p),
+                ("Cm", c_void_p), ("D", c_void_p), ("h0", c_void_p), ("y", c_void_p)]
+
+
 _lib = None
 
 
@@ -63,12 +69,14 @@ def lib() -> ctypes.CDLL:
         A, C = ctypes.POINTER(TdAttnArgs), ctypes.POINTER(TdCommitArgs)
         P = ctypes.POINTER(TdAppendArgs)
         LH = ctypes.POINTER(TdLmheadArgs)
+        MB = ctypes.POINTER(TdMambaArgs)
         sig = {
             "td_abi_version": (c_uint32, []),
             "td_sizeof_attn_args": (c_size_t, []),
             "td_sizeof_commit_args": (c_size_t, []),
             "td_sizeof_append_args": (c_size_t, []),
             "td_sizeof_lmhead_args": (c_size_t, []),
+            "td_sizeof_mamba_args": (c_size_t, []),
             "td_status_str": (ctypes.c_char_p, [c_int]),
             "td_attn_workspace_bytes": (c_size_t, [A]),
             "td_commit_workspace_bytes": (c_size_t, [C]),
@@ -80,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "td_cache_append": (c_int, [P, c_void_p]),
             "td_lmhead_commit_workspace_bytes": (c_size_t, [LH]),
             "td_lmhead_commit": (c_int, [LH, c_void_p, c_size_t, c_void_p]),
+            "td_mamba_block_scan": (c_int, [MB, c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -87,7 +96,8 @@ def lib() -> ctypes.CDLL:
         if L.td_sizeof_attn_args() != ctypes.sizeof(TdAttnArgs) or \
                 L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs) or \
                 L.td_sizeof_append_args() != ctypes.sizeof(TdAppendArgs) or \
-                L.td_sizeof_lmhead_args() != ctypes.sizeof(TdLmheadArgs):
+                L.td_sizeof_lmhead_args() != ctypes.sizeof(TdLmheadArgs) or \
+                L.td_sizeof_mamba_args() != ctypes.sizeof(TdMambaArgs):
             raise RuntimeError("libtd.so struct layout does not match the binding")
         _lib = L
     return _lib
@@ -230,6 +240,23 @@ def lmhead_args(hidden, w_head, commit, token, gamma, masked_in=None, maxprob=No
     return a
 
 
+def mamba_args(x, dt, A, Bm, Cm, D, h0, y) -> TdMambaArgs:
+    torch = _torch()
+    B, S, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    a = TdMambaArgs()
+    a.B, a.S, a.H, a.P, a.N, a.G = B, S, H, P, N, G
+    a.x = _ptr(x, "x", torch.bfloat16)
+    a.dt = _ptr(dt, "dt", torch.float32, (B, S, H))
+    a.A = _ptr(A, "A", torch.float32, (H,))
+    a.Bm = _ptr(Bm, "Bm", torch.bfloat16, (B, S, G, N))
+    a.Cm = _ptr(Cm, "Cm", torch.bfloat16, (B, S, G, N))
+    a.D = _ptr(D, "D", torch.float32, (H,))
+    a.h0 = _ptr(h0, "h0", torch.float32, (B, H, P, N))
+    a.y = _ptr(y, "y", torch.bfloat16, (B, S, H, P))
+    return a
+
+
 class Workspace:
     """Caller-owned device scratch for the td_* calls (a torch byte tensor,
     grown on demand; torch's allocator returns 256-byte aligned blocks)."""
@@ -329,4 +356,13 @@ def td_lmhead_commit(hidden, w_head, commit, token, *, gamma, masked_in=None, ma
     need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
     ptr, n = _ws(workspace, hidden.device).get(need)
     check(L.td_lmhead_commit(ctypes.byref(a), ptr, n, _stream(stream)), "td_lmhead_commit")
+
+
+def td_mamba_block_scan(x, dt, A, Bm, Cm, D, h0, y, *, stream=None):
+    """The state-space core of a denoiser Mamba-2 layer over the block,
+    started from the context tower's state h0 [B, H, P, N]; writes y."""
+    L = lib()
+    a = mamba_args(x, dt, A, Bm, Cm, D, h0, y)
+    check(L.td_mamba_block_scan(ctypes.byref(a), _stream(stream)), "td_mamba_block_scan")
+    return y
 

@@ -1,7 +1,7 @@
 // extern "C" entry points of libtd.so (declared and documented in td.h).
 // Validation and planning happen here, on the host, before anything is
 // enqueued; the launchers live in td_attn.hip / td_commit.hip / td_lmhead.hip /
-// td_append.hip.
+// td_mamba.hip / td_append.hip.
 #include <stdint.h>
 
 #include "td_internal.h"
@@ -47,6 +47,7 @@ size_t td_sizeof_attn_args(void) { return sizeof(td_attn_args); }
 size_t td_sizeof_commit_args(void) { return sizeof(td_commit_args); }
 size_t td_sizeof_append_args(void) { return sizeof(td_append_args); }
 size_t td_sizeof_lmhead_args(void) { return sizeof(td_lmhead_args); }
+size_t td_sizeof_mamba_args(void) { return sizeof(td_mamba_args); }
 
 const char *td_status_str(int status) {
   switch (status) {
@@ -114,6 +115,12 @@ int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stre
   rc = check_ws(lmhead_ws_bytes(a), ws, ws_bytes);
   if (rc != TD_OK) return rc;
   return launch_lmhead(a, ws, stream);
+}
+
+int td_mamba_block_scan(const td_mamba_args *a, td_stream_t stream) {
+  const int rc = validate_mamba(a);
+  if (rc != TD_OK) return rc;
+  return launch_mamba(a, stream);
 }
 
 int td_cache_append(const td_append_args *p, td_stream_t stream) {

@@ -57,6 +57,7 @@ int validate_attn(const td_attn_args *a, bool check_ptrs);
 int validate_commit(const td_commit_args *c, bool check_ptrs);
 int validate_append(const td_append_args *p);
 int validate_lmhead(const td_lmhead_args *a, bool check_ptrs);
+int validate_mamba(const td_mamba_args *a);
 AttnPlan plan_attn(const td_attn_args *a);
 CommitPlan plan_commit(const td_commit_args *c);
 
@@ -86,5 +87,6 @@ inline size_t lmhead_ws_bytes(const td_lmhead_args *a) {
   return align256(lmhead_parts_bytes(a)) + align256(M * sizeof(Part)) + (M + 1) * sizeof(int32_t);
 }
 int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream);
+int launch_mamba(const td_mamba_args *a, void *stream);
 
 }  // namespace td

@@ -115,6 +115,20 @@ int validate_lmhead(const td_lmhead_args *a, bool check_ptrs) {
   return TD_OK;
 }
 
+int validate_mamba(const td_mamba_args *a) {
+  if (!a) return TD_ERR_INVALID;
+  if (a->B < 1 || a->S < 1 || a->H < 1 || a->P < 1 || a->N < 1 || a->G < 1) return TD_ERR_INVALID;
+  if (a->H % a->G != 0) return TD_ERR_INVALID;
+  if (a->S > 16) return TD_ERR_UNSUPPORTED;
+  if (a->P != 16 && a->P != 32 && a->P != 64 && a->P != 128) return TD_ERR_UNSUPPORTED;
+  if (a->N % 32 != 0 || a->N > 1024) return TD_ERR_UNSUPPORTED;
+  if (int64_t(a->B) * a->H > (int64_t(1) << 31) - 4) return TD_ERR_UNSUPPORTED;
+  if (!a->x || !a->dt || !a->A || !a->Bm || !a->Cm || !a->D || !a->h0 || !a->y) return TD_ERR_INVALID;
+  if (!aligned16(a->x) || !aligned16(a->Bm) || !aligned16(a->Cm) || !aligned16(a->h0)) return TD_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(a->y) & 7u) return TD_ERR_INVALID;
+  return TD_OK;
+}
+
 static int grid_override() {
   const char *env = getenv("TD_ATTN_GRID");
   if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);

@@ -198,12 +198,42 @@ typedef struct {
   int32_t *n_masked_left;  /* out [1] or NULL                                  */
 } td_lmhead_args;
 
+/*
+ * State-space core of one denoiser Mamba-2 layer over the block, its state
+ * seeded from the context tower (chathome, inference paragraph: the
+ * denoiser's Mamba-2 layers start from the context tower's state).  The
+ * recurrence is Mamba-2's selective scan with one decay rate per head; for
+ * sequence b, head h (group g = h / (H/G)) and tokens t = 0 .. S-1:
+ *   st <- exp(dt[b,t,h] * A[h]) * st + dt[b,t,h] * x[b,t,h,:] (outer) Bm[b,t,g,:]
+ *   y[b,t,h,:] = st . Cm[b,t,g,:] + D[h] * x[b,t,h,:]
+ * with st = h0[b,h] before the first token.  Computed in fp32; y rounded to
+ * bf16.  The state after the block is not returned (on the denoise path the
+ * context tower recomputes it from the committed tokens).
+ */
+typedef struct {
+  int32_t B;               /* sequences, >= 1                                  */
+  int32_t S;               /* block tokens, 1 .. 16                            */
+  int32_t H;               /* SSM heads, >= 1, a multiple of G                 */
+  int32_t P;               /* head dim: 16, 32, 64 or 128                      */
+  int32_t N;               /* state size: a multiple of 32, 32 .. 1024         */
+  int32_t G;               /* groups of Bm / Cm, >= 1                          */
+  const void *x;           /* [B, S, H, P] bf16                                */
+  const float *dt;         /* [B, S, H] step sizes                             */
+  const float *A;          /* [H] decay rates (negative)                       */
+  const void *Bm;          /* [B, S, G, N] bf16 input projections              */
+  const void *Cm;          /* [B, S, G, N] bf16 output projections             */
+  const float *D;          /* [H] skip weights                                 */
+  const float *h0;         /* [B, H, P, N] fp32 seed state                     */
+  void *y;                 /* out [B, S, H, P] bf16                            */
+} td_mamba_args;
+
 /* Library identity and struct sizes, for bindings to check their layout. */
 uint32_t td_abi_version(void);
 size_t td_sizeof_attn_args(void);
 size_t td_sizeof_commit_args(void);
 size_t td_sizeof_append_args(void);
 size_t td_sizeof_lmhead_args(void);
+size_t td_sizeof_mamba_args(void);
 const char *td_status_str(int status);
 
 /* Workspace each call needs, in bytes (0 when none).  Pure host functions:
@@ -252,6 +282,10 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
  * slice of the vocabulary), 16 per position and the list of eligible
  * positions.  Returns a td_status. */
 int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* Mamba-2 block scan (see td_mamba_args).  Needs no workspace.  x, Bm, Cm
+ * and h0 must be 16-byte aligned, y 8-byte aligned.  Returns a td_status. */
+int td_mamba_block_scan(const td_mamba_args *a, td_stream_t stream);
 
 /* Context-cache append (see td_append_args).  Needs no workspace.  Every
  * data pointer must be 16-byte aligned; no output may overlap an input or the

@@ -31,6 +31,7 @@ def test_struct_layout_and_version(L):
     assert L.td_sizeof_commit_args() == ctypes.sizeof(_td.TdCommitArgs)
     assert L.td_sizeof_append_args() == ctypes.sizeof(_td.TdAppendArgs)
     assert L.td_sizeof_lmhead_args() == ctypes.sizeof(_td.TdLmheadArgs)
+    assert L.td_sizeof_mamba_args() == ctypes.sizeof(_td.TdMambaArgs)
     for rc in (0, -1, -2, -3, -4, 7):
         assert isinstance(td.status_str(rc), str)
 
@@ -244,4 +245,27 @@ def test_lmhead_workspace_bytes(L):
     assert L.td_lmhead_commit_workspace_bytes(ctypes.byref(lmhead(H=100))) == 0
     need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
     assert L.td_lmhead_commit(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+
+
+def mamba(**kw):
+    a = _td.TdMambaArgs()
+    a.B, a.S, a.H, a.P, a.N, a.G = 64, 16, 128, 64, 128, 8
+    a.x, a.dt, a.A, a.Bm, a.Cm, a.D, a.h0, a.y = (k * GB for k in range(1, 9))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(H=0), INVALID), (dict(G=0), INVALID),
+    (dict(H=12, G=8), INVALID), (dict(S=17), UNSUPPORTED), (dict(P=48), UNSUPPORTED),
+    (dict(P=256), UNSUPPORTED), (dict(N=100), UNSUPPORTED), (dict(N=48), UNSUPPORTED),
+    (dict(N=2048), UNSUPPORTED),
+    (dict(x=None), INVALID), (dict(h0=None), INVALID), (dict(y=None), INVALID), (dict(dt=None), INVALID),
+    (dict(Bm=2 * GB + 8), INVALID), (dict(h0=7 * GB + 4), INVALID), (dict(y=8 * GB + 2), INVALID),
+    (dict(x=1 * GB + 8), INVALID),
+])
+def test_mamba_validation(L, kw, rc):
+    a = mamba(**kw)
+    assert L.td_mamba_block_scan(ctypes.byref(a), None) == rc
 

@@ -65,3 +65,12 @@ def test_algorithmic_bytes_of_the_cache_append():
     # K and V rows of 2 x 128 bf16 (512 B each), read once and written once,
     # for the 300,000 old rows and the 64 x 16 new ones; offsets read + written
     assert bench.append_algorithmic(w, 300000) == 4 * (300000 + 1024) * 512 + 16 * 65
+
+
+def test_algorithmic_bytes_of_the_mamba_scan():
+    import synth
+    w = synth.MAMBA_WORKLOADS["mamba_b64_s16_h128"]
+    state = 64 * 128 * 64 * 128 * 4                      # fp32 seed states
+    xy = 2 * 64 * 16 * 128 * 64 * 2                      # x in, y out (bf16)
+    bc = 2 * 64 * 16 * 8 * 128 * 2                       # Bm, Cm (bf16)
+    assert bench.mamba_algorithmic(w) == state + xy + bc + 64 * 16 * 128 * 4 + 2 * 128 * 4

@@ -13,4 +13,5 @@ from .td_oracle import (  # noqa: F401
     lmhead_logits,
     lmhead_commit,
     mamba_block_scan,
+    adaln_modulate,
 )

@@ -258,3 +258,41 @@ def mamba_block_scan(x, dt, A, Bm, Cm, D, h0):
             hs[b, h] = st
     return y, hs
 
+
+def adaln_modulate(x, f, t_mod, tab_gate, tab_shift, tab_scale, w_norm, eps):
+    """adaLN-single time conditioning between two denoiser layers ([chathome]
+    inference paragraph: the diffusion timestep modulates every layer through
+    adaLN-single, a module of about 1.5M parameters).
+
+    Reading (the pages name the scheme only; this is adaLN-single as
+    PixArt-alpha defines it): one shared projection of the timestep gives
+    every sequence three vectors, shift / scale / gate (t_mod rows 0, 1, 2),
+    and each layer adds its own learned [3, H] table to them.  Layer l's
+    output f joins the residual stream through its gate; layer l + 1 then
+    reads the RMS-normalised stream, scaled by (1 + its scale) and moved by
+    its shift:
+        r = x + (t_mod[b, 2] + tab_gate) * f              (f given)
+        r = x                                             (f None)
+        h = r / sqrt(mean_j r_j^2 + eps) * w_norm * (1 + t_mod[b, 1] + tab_scale)
+              + (t_mod[b, 0] + tab_shift)
+    x, f [B, S, H]; t_mod [B, 3, H]; tab_* and w_norm [H] (None: zero tables,
+    unit weight).  Returns (r, h) in float64, unrounded."""
+    x = np.asarray(x, dtype=np.float64)
+    nb, S, H = x.shape
+    t_mod = np.asarray(t_mod, dtype=np.float64)
+
+    def row(v, fill):
+        return np.full(H, fill) if v is None else np.asarray(v, dtype=np.float64)
+
+    shift = t_mod[:, 0, :] + row(tab_shift, 0.0)         # [B, H]
+    scale = t_mod[:, 1, :] + row(tab_scale, 0.0)
+    gate = t_mod[:, 2, :] + row(tab_gate, 0.0)
+    w = row(w_norm, 1.0)
+    if f is None:
+        r = x.copy()
+    else:
+        r = x + gate[:, None, :] * np.asarray(f, dtype=np.float64)
+    rms = np.sqrt(np.mean(r * r, axis=2, keepdims=True) + eps)
+    h = r / rms * w * (1.0 + scale[:, None, :]) + shift[:, None, :]
+    return r, h
+

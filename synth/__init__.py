@@ -7,6 +7,8 @@ oracle consumes the arrays it returns after an exact upcast to float64, the
 HIP path consumes the very same bits on the device.
 """
 from .workloads import (  # noqa: F401
+    ADALN_WORKLOADS,
+    AdalnWorkload,
     LMHEAD_WORKLOADS,
     LMHeadWorkload,
     MAMBA_WORKLOADS,
@@ -16,6 +18,7 @@ from .workloads import (  # noqa: F401
     bf16_bits_to_f32,
     bf16_bits_to_f64,
     f32_to_bf16_bits,
+    make_adaln_inputs,
     make_attention_inputs,
     make_commit_inputs,
     make_lmhead_inputs,

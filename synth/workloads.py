@@ -357,3 +357,54 @@ def make_mamba_inputs(w: MambaWorkload, seed: int) -> dict:
     return dict(x=f32_to_bf16_bits(x), dt=dt, A=A, Bm=f32_to_bf16_bits(Bm), Cm=f32_to_bf16_bits(Cm),
                 D=D, h0=h0)
 
+
+
+# ----------------------------------------------------------------------------
+# adaLN-single modulation inputs
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AdalnWorkload:
+    name: str
+    B: int
+    S: int
+    H: int               # hidden size
+    exact: bool = False  # grid values: the gated sum is exact in fp32
+
+    def with_(self, **kw) -> "AdalnWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# Hidden size 4096 is assumed (the pages give none), as for the LM head.
+ADALN_WORKLOADS: dict[str, AdalnWorkload] = {
+    "adaln_b4_s16_h256": AdalnWorkload("adaln_b4_s16_h256", B=4, S=16, H=256),
+    "adaln_exact_b4_s16_h256": AdalnWorkload("adaln_exact_b4_s16_h256", B=4, S=16, H=256, exact=True),
+    "adaln_b64_s16_h4096": AdalnWorkload("adaln_b64_s16_h4096", B=64, S=16, H=4096),
+}
+
+
+def make_adaln_inputs(w: AdalnWorkload, seed: int) -> dict:
+    """x, f [B,S,H] as bf16 bits; t_mod [B,3,H] (shift, scale, gate),
+    tab_gate / tab_shift / tab_scale and w_norm [H] in float32.  Realistic
+    draws: x N(0, 2^2) (the residual stream), f N(0,1), t_mod N(0, 0.3^2),
+    tables N(0, 0.1^2), w_norm U(0.5, 1.5).  Exact draws: x and f on the 1/64
+    grid in (-4, 4), the gate rows of t_mod and the table on the 1/32 grid in
+    [-1, 1], so that x + gate * f is exact in fp32.  Draw order: x, f, t_mod,
+    tab_gate, tab_shift, tab_scale, w_norm."""
+    rng = np.random.default_rng([seed, 17])
+    B, S, H = w.B, w.S, w.H
+    if w.exact:
+        x = rng.integers(-255, 256, (B, S, H)).astype(np.float32) / 64
+        f = rng.integers(-255, 256, (B, S, H)).astype(np.float32) / 64
+        t_mod = _normal(rng, (B, 3, H), 0.3)
+        t_mod[:, 2, :] = rng.integers(-32, 33, (B, H)).astype(np.float32) / 32
+        tab_gate = rng.integers(-32, 33, H).astype(np.float32) / 32
+    else:
+        x = _normal(rng, (B, S, H), 2.0)
+        f = _normal(rng, (B, S, H), 1.0)
+        t_mod = _normal(rng, (B, 3, H), 0.3)
+        tab_gate = _normal(rng, H, 0.1)
+    tab_shift = _normal(rng, H, 0.1)
+    tab_scale = _normal(rng, H, 0.1)
+    w_norm = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    return dict(x=f32_to_bf16_bits(x), f=f32_to_bf16_bits(f), t_mod=t_mod, tab_gate=tab_gate,
+                tab_shift=tab_shift, tab_scale=tab_scale, w_norm=w_norm)

@@ -781,3 +781,151 @@ def pin_mamba_groups(scan):
 MAMBA_PINS = [pin_mamba_closed_form, pin_mamba_zero_step, pin_mamba_no_decay, pin_mamba_state_passing,
               pin_mamba_brute, pin_mamba_groups]
 
+
+# ----------------------------------------------------------------------------
+# adaLN-single modulation between layers ([chathome] inference paragraph)
+# ----------------------------------------------------------------------------
+def _ada_inputs(seed, B=3, S=4, H=8, with_f=True, tables=True, eps=1e-5):
+    rng = np.random.default_rng(seed)
+    return dict(
+        x=rng.standard_normal((B, S, H)) * 2.0,
+        f=rng.standard_normal((B, S, H)) if with_f else None,
+        t_mod=rng.standard_normal((B, 3, H)) * 0.5,
+        tab_gate=rng.standard_normal(H) * 0.3 if tables else None,
+        tab_shift=rng.standard_normal(H) * 0.3 if tables else None,
+        tab_scale=rng.standard_normal(H) * 0.3 if tables else None,
+        w_norm=rng.uniform(0.5, 1.5, H) if tables else None,
+        eps=eps)
+
+
+def _call_ada(fn, a):
+    return fn(a["x"], a["f"], a["t_mod"], a["tab_gate"], a["tab_shift"], a["tab_scale"],
+              a["w_norm"], a["eps"])
+
+
+def pin_adaln_rmsnorm_library(fn):
+    """No residual and no modulation: h is torch's own RMSNorm (float64)."""
+    a = _ada_inputs(71, with_f=False)
+    a["t_mod"] = np.zeros_like(a["t_mod"])
+    a["tab_gate"] = a["tab_shift"] = a["tab_scale"] = None
+    r, h = _call_ada(fn, a)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(a["x"]), (a["x"].shape[-1],),
+                                       weight=torch.from_numpy(a["w_norm"]), eps=a["eps"]).numpy()
+    assert np.allclose(h, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r, a["x"])
+
+
+def pin_adaln_closed_form(fn):
+    """Rows of +-c (every |r_j| = c, eps = 0) normalise to +-1, so
+    h_j = sign_j w_j (1 + scale_j) + shift_j exactly, for any c > 0."""
+    B, S, H = 2, 3, 6
+    rng = np.random.default_rng(72)
+    sign = rng.choice([-1.0, 1.0], (B, S, H))
+    c = np.array([0.25, 3.0, 40.0])[None, :, None]
+    x = sign * c
+    t_mod = rng.standard_normal((B, 3, H))
+    w = rng.uniform(0.5, 2.0, H)
+    r, h = fn(x, None, t_mod, None, None, None, w, 0.0)
+    ref = sign * w * (1.0 + t_mod[:, 1][:, None, :]) + t_mod[:, 0][:, None, :]
+    assert np.allclose(h, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_adaln_gate_cases(fn):
+    """Gate 0 leaves the stream alone (r = x, h as with no residual); gate 1
+    with f = -x empties the row, whose normalised value is then 0 and h is the
+    shift alone; a gate of g with f = x scales the row by 1 + g, which the
+    norm removes (g > -1, eps = 0)."""
+    a = _ada_inputs(73)
+    a["t_mod"][:, 2, :] = 0.0
+    a["tab_gate"] = np.zeros_like(a["tab_gate"])
+    r0, h0 = _call_ada(fn, a)
+    b = dict(a, f=None)
+    r1, h1 = _call_ada(fn, b)
+    assert np.array_equal(r0, a["x"]) and np.allclose(h0, h1, rtol=1e-13, atol=1e-13)
+    c = dict(a, f=-a["x"])
+    c["t_mod"] = a["t_mod"].copy()
+    c["t_mod"][:, 2, :] = 1.0
+    r2, h2 = _call_ada(fn, c)
+    shift = a["t_mod"][:, 0, :] + a["tab_shift"]
+    assert np.allclose(r2, 0.0, atol=1e-15)
+    assert np.allclose(h2, np.broadcast_to(shift[:, None, :], h2.shape), rtol=1e-13, atol=1e-13)
+    d = dict(c, f=a["x"], eps=0.0)
+    d["t_mod"] = c["t_mod"].copy()
+    d["t_mod"][:, 2, :] = 0.75
+    r3, h3 = _call_ada(fn, d)
+    r4, h4 = _call_ada(fn, dict(d, f=None))
+    assert np.allclose(r3, 1.75 * a["x"], rtol=1e-14, atol=1e-14)
+    assert np.allclose(h3, h4, rtol=1e-12, atol=1e-12)
+
+
+def pin_adaln_scale_invariance(fn):
+    """RMSNorm with eps = 0 ignores the row's scale: x and c x (c > 0) give
+    the same h; -x gives -h when the shift is zero."""
+    a = _ada_inputs(74, with_f=False, eps=0.0)
+    _, h = _call_ada(fn, a)
+    _, hc = _call_ada(fn, dict(a, x=a["x"] * 7.5))
+    assert np.allclose(h, hc, rtol=1e-12, atol=1e-12)
+    z = dict(a, tab_shift=None)
+    z["t_mod"] = a["t_mod"].copy()
+    z["t_mod"][:, 0, :] = 0.0
+    _, hp = _call_ada(fn, z)
+    _, hn = _call_ada(fn, dict(z, x=-a["x"]))
+    assert np.allclose(hn, -hp, rtol=1e-13, atol=1e-13)
+
+
+def pin_adaln_only_sum_matters(fn):
+    """A layer's modulation is the shared vector plus the layer's table: moving
+    any amount between the two changes nothing."""
+    a = _ada_inputs(75)
+    r, h = _call_ada(fn, a)
+    rng = np.random.default_rng(76)
+    delta = rng.standard_normal((3, a["x"].shape[-1]))
+    b = dict(a, t_mod=a["t_mod"] + delta[None], tab_shift=a["tab_shift"] - delta[0],
+             tab_scale=a["tab_scale"] - delta[1], tab_gate=a["tab_gate"] - delta[2])
+    r2, h2 = _call_ada(fn, b)
+    assert np.allclose(r, r2, rtol=1e-12, atol=1e-12) and np.allclose(h, h2, rtol=1e-12, atol=1e-12)
+
+
+def pin_adaln_per_sequence(fn):
+    """Each sequence reads its own timestep vectors: permuting the sequences
+    (inputs and t_mod together) permutes the outputs; the positions of one
+    sequence do not interact (changing one position leaves the others)."""
+    a = _ada_inputs(77, B=4)
+    r, h = _call_ada(fn, a)
+    perm = np.array([2, 0, 3, 1])
+    b = dict(a, x=a["x"][perm], f=a["f"][perm], t_mod=a["t_mod"][perm])
+    r2, h2 = _call_ada(fn, b)
+    assert np.allclose(r2, r[perm], rtol=1e-14, atol=1e-14)
+    assert np.allclose(h2, h[perm], rtol=1e-14, atol=1e-14)
+    c = dict(a, x=a["x"].copy())
+    c["x"][1, 2] += 5.0
+    r3, h3 = _call_ada(fn, c)
+    keep = np.ones(a["x"].shape[:2], bool)
+    keep[1, 2] = False
+    assert np.array_equal(h3[keep], h[keep]) and not np.allclose(h3[1, 2], h[1, 2])
+
+
+def pin_adaln_brute(fn):
+    """Pure-Python loops on a tiny case."""
+    a = _ada_inputs(78, B=2, S=2, H=3)
+    r, h = _call_ada(fn, a)
+    for b in range(2):
+        for s in range(2):
+            rr = []
+            for j in range(3):
+                g = float(a["t_mod"][b, 2, j]) + float(a["tab_gate"][j])
+                rr.append(float(a["x"][b, s, j]) + g * float(a["f"][b, s, j]))
+            ms = sum(v * v for v in rr) / 3.0
+            inv = 1.0 / math.sqrt(ms + a["eps"])
+            for j in range(3):
+                sc = 1.0 + float(a["t_mod"][b, 1, j]) + float(a["tab_scale"][j])
+                sh = float(a["t_mod"][b, 0, j]) + float(a["tab_shift"][j])
+                want = rr[j] * inv * float(a["w_norm"][j]) * sc + sh
+                assert abs(r[b, s, j] - rr[j]) <= 1e-12
+                assert abs(h[b, s, j] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+ADALN_PINS = [pin_adaln_rmsnorm_library, pin_adaln_closed_form, pin_adaln_gate_cases,
+              pin_adaln_scale_invariance, pin_adaln_only_sum_matters, pin_adaln_per_sequence,
+              pin_adaln_brute]
+

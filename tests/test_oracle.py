@@ -48,3 +48,8 @@ def test_lmhead_commit_pin(pin):
 @pytest.mark.parametrize("pin", pins.MAMBA_PINS, ids=lambda f: f.__name__)
 def test_mamba_pin(pin):
     pin(oracle.mamba_block_scan)
+
+
+@pytest.mark.parametrize("pin", pins.ADALN_PINS, ids=lambda f: f.__name__)
+def test_adaln_pin(pin):
+    pin(oracle.adaln_modulate)

@@ -63,6 +63,15 @@ MUTANTS = [
     ("mamba_output_from_seed", "y[b, t, h] = st @ Cm[b, t, grp]", "y[b, t, h] = hs[b, h] @ Cm[b, t, grp]"),
     ("mamba_no_skip", "y[b, t, h] = st @ Cm[b, t, grp] + D[h] * x[b, t, h]", "y[b, t, h] = st @ Cm[b, t, grp]"),
     ("mamba_b_for_c", "np.outer(x[b, t, h], Bm[b, t, grp])", "np.outer(x[b, t, h], Cm[b, t, grp])"),
+    ("adaln_layernorm", "rms = np.sqrt(np.mean(r * r, axis=2, keepdims=True) + eps)",
+     "rms = np.sqrt(np.var(r, axis=2, keepdims=True) + eps)"),
+    ("adaln_scale_without_one", "* w * (1.0 + scale[:, None, :])", "* w * scale[:, None, :]"),
+    ("adaln_eps_outside_sqrt", "np.sqrt(np.mean(r * r, axis=2, keepdims=True) + eps)",
+     "np.sqrt(np.mean(r * r, axis=2, keepdims=True)) + eps"),
+    ("adaln_gate_from_scale_row", "gate = t_mod[:, 2, :]", "gate = t_mod[:, 1, :]"),
+    ("adaln_table_ignored", "shift = t_mod[:, 0, :] + row(tab_shift, 0.0)", "shift = t_mod[:, 0, :]"),
+    ("adaln_norm_of_x", "rms = np.sqrt(np.mean(r * r, axis=2", "rms = np.sqrt(np.mean(x * x, axis=2"),
+    ("adaln_norm_over_tokens", "np.mean(r * r, axis=2, keepdims=True)", "np.mean(r * r, axis=(1, 2), keepdims=True)"),
     ("append_new_rows_truncated", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b, 1:]]"),
 ]
 
@@ -86,6 +95,7 @@ def _all_pins(mod):
     yield from ((p, mod.lmhead_logits) for p in pins.LMHEAD_LOGIT_PINS)
     yield from ((p, mod.lmhead_commit) for p in pins.LMHEAD_PINS)
     yield from ((p, mod.mamba_block_scan) for p in pins.MAMBA_PINS)
+    yield from ((p, mod.adaln_modulate) for p in pins.ADALN_PINS)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

@@ -82,3 +82,24 @@ def test_mamba_inputs_deterministic_and_ranged():
     assert a["h0"].dtype == np.float32 and a["dt"].dtype == np.float32
     assert (a["dt"] >= 1e-3 * 0.999).all() and (a["dt"] <= 0.1 * 1.001).all()
     assert (a["A"] <= -1.0 + 1e-6).all() and (a["A"] >= -16.0 - 1e-4).all()
+
+
+def test_adaln_inputs_deterministic_and_exact_grid():
+    w = synth.ADALN_WORKLOADS["adaln_exact_b4_s16_h256"]
+    a = synth.make_adaln_inputs(w, 3)
+    b = synth.make_adaln_inputs(w, 3)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert a["x"].shape == (4, 16, 256) and a["x"].dtype == np.uint16
+    assert a["t_mod"].shape == (4, 3, 256) and a["t_mod"].dtype == np.float32
+    x = synth.bf16_bits_to_f64(a["x"])
+    f = synth.bf16_bits_to_f64(a["f"])
+    assert np.array_equal(x * 64, np.round(x * 64)) and np.abs(x).max() < 4
+    assert np.array_equal(f * 64, np.round(f * 64))
+    g = a["t_mod"][:, 2, :].astype(np.float64)[:, None, :] + a["tab_gate"].astype(np.float64)
+    r = x + g * f
+    # the gated sum is exact in fp32: fp32 arithmetic reproduces it
+    r32 = np.float32(x) + (np.float32(a["t_mod"][:, 2, :])[:, None, :] + a["tab_gate"]) * np.float32(f)
+    assert np.array_equal(r32.astype(np.float64), r)
+    c = synth.make_adaln_inputs(synth.ADALN_WORKLOADS["adaln_b4_s16_h256"], 3)
+    assert abs(synth.bf16_bits_to_f64(c["x"]).std() - 2.0) < 0.1

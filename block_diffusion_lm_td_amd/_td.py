@@ -56,6 +56,13 @@ class TdMambaArgs(ctypes.Structure):
                 ("Cm", c_void_p), ("D", c_void_p), ("h0", c_void_p), ("y", c_void_p)]
 
 
+class TdAdalnArgs(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("H", c_int32), ("eps", ctypes.c_float),
+                ("x", c_void_p), ("f", c_void_p), ("t_mod", c_void_p), ("tab_gate", c_void_p),
+                ("tab_shift", c_void_p), ("tab_scale", c_void_p), ("w_norm", c_void_p),
+                ("r_out", c_void_p), ("h", c_void_p)]
+
+
 _lib = None
 
 
@@ -70,6 +77,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(TdAppendArgs)
         LH = ctypes.POINTER(TdLmheadArgs)
         MB = ctypes.POINTER(TdMambaArgs)
+        AD = ctypes.POINTER(TdAdalnArgs)
         sig = {
             "td_abi_version": (c_uint32, []),
             "td_sizeof_attn_args": (c_size_t, []),
@@ -77,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "td_sizeof_append_args": (c_size_t, []),
             "td_sizeof_lmhead_args": (c_size_t, []),
             "td_sizeof_mamba_args": (c_size_t, []),
+            "td_sizeof_adaln_args": (c_size_t, []),
             "td_status_str": (ctypes.c_char_p, [c_int]),
             "td_attn_workspace_bytes": (c_size_t, [A]),
             "td_commit_workspace_bytes": (c_size_t, [C]),
@@ -89,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "td_lmhead_commit_workspace_bytes": (c_size_t, [LH]),
             "td_lmhead_commit": (c_int, [LH, c_void_p, c_size_t, c_void_p]),
             "td_mamba_block_scan": (c_int, [MB, c_void_p]),
+            "td_adaln_modulate": (c_int, [AD, c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -97,7 +107,8 @@ def lib() -> ctypes.CDLL:
                 L.td_sizeof_commit_args() != ctypes.sizeof(TdCommitArgs) or \
                 L.td_sizeof_append_args() != ctypes.sizeof(TdAppendArgs) or \
                 L.td_sizeof_lmhead_args() != ctypes.sizeof(TdLmheadArgs) or \
-                L.td_sizeof_mamba_args() != ctypes.sizeof(TdMambaArgs):
+                L.td_sizeof_mamba_args() != ctypes.sizeof(TdMambaArgs) or \
+                L.td_sizeof_adaln_args() != ctypes.sizeof(TdAdalnArgs):
             raise RuntimeError("libtd.so struct layout does not match the binding")
         _lib = L
     return _lib
@@ -257,6 +268,24 @@ def mamba_args(x, dt, A, Bm, Cm, D, h0, y) -> TdMambaArgs:
     return a
 
 
+def adaln_args(x, f, t_mod, h, r_out=None, *, tab_gate=None, tab_shift=None, tab_scale=None,
+               w_norm=None, eps=1e-5) -> TdAdalnArgs:
+    torch = _torch()
+    B, S, H = x.shape
+    a = TdAdalnArgs()
+    a.B, a.S, a.H, a.eps = B, S, H, float(eps)
+    a.x = _ptr(x, "x", torch.bfloat16)
+    a.f = _ptr(f, "f", torch.bfloat16, (B, S, H))
+    a.t_mod = _ptr(t_mod, "t_mod", torch.float32, (B, 3, H))
+    a.tab_gate = _ptr(tab_gate, "tab_gate", torch.float32, (H,))
+    a.tab_shift = _ptr(tab_shift, "tab_shift", torch.float32, (H,))
+    a.tab_scale = _ptr(tab_scale, "tab_scale", torch.float32, (H,))
+    a.w_norm = _ptr(w_norm, "w_norm", torch.float32, (H,))
+    a.r_out = _ptr(r_out, "r_out", torch.bfloat16, (B, S, H))
+    a.h = _ptr(h, "h", torch.bfloat16, (B, S, H))
+    return a
+
+
 class Workspace:
     """Caller-owned device scratch for the td_* calls (a torch byte tensor,
     grown on demand; torch's allocator returns 256-byte aligned blocks)."""
@@ -365,4 +394,16 @@ def td_mamba_block_scan(x, dt, A, Bm, Cm, D, h0, y, *, stream=None):
     a = mamba_args(x, dt, A, Bm, Cm, D, h0, y)
     check(L.td_mamba_block_scan(ctypes.byref(a), _stream(stream)), "td_mamba_block_scan")
     return y
+
+
+def td_adaln_modulate(x, f, t_mod, h, r_out=None, *, tab_gate=None, tab_shift=None,
+                      tab_scale=None, w_norm=None, eps=1e-5, stream=None):
+    """adaLN-single between two layers: r = x + gate * f (written to r_out
+    when f is given), h = RMSNorm(r) * w_norm * (1 + scale) + shift, with
+    shift / scale / gate = t_mod [B, 3, H] rows plus the layer tables."""
+    L = lib()
+    a = adaln_args(x, f, t_mod, h, r_out, tab_gate=tab_gate, tab_shift=tab_shift,
+                   tab_scale=tab_scale, w_norm=w_norm, eps=eps)
+    check(L.td_adaln_modulate(ctypes.byref(a), _stream(stream)), "td_adaln_modulate")
+    return h
 

@@ -1,7 +1,7 @@
 // extern "C" entry points of libtd.so (declared and documented in td.h).
 // Validation and planning happen here, on the host, before anything is
 // enqueued; the launchers live in td_attn.hip / td_commit.hip / td_lmhead.hip /
-// td_mamba.hip / td_append.hip.
+// td_mamba.hip / td_adaln.hip / td_append.hip.
 #include <stdint.h>
 
 #include "td_internal.h"
@@ -48,6 +48,7 @@ size_t td_sizeof_commit_args(void) { return sizeof(td_commit_args); }
 size_t td_sizeof_append_args(void) { return sizeof(td_append_args); }
 size_t td_sizeof_lmhead_args(void) { return sizeof(td_lmhead_args); }
 size_t td_sizeof_mamba_args(void) { return sizeof(td_mamba_args); }
+size_t td_sizeof_adaln_args(void) { return sizeof(td_adaln_args); }
 
 const char *td_status_str(int status) {
   switch (status) {
@@ -121,6 +122,13 @@ int td_mamba_block_scan(const td_mamba_args *a, td_stream_t stream) {
   const int rc = validate_mamba(a);
   if (rc != TD_OK) return rc;
   return launch_mamba(a, stream);
+}
+
+int td_adaln_modulate(const td_adaln_args *a, td_stream_t stream) {
+  const int rc = validate_adaln(a);
+  if (rc != TD_OK) return rc;
+  if (int64_t(a->B) * a->S == 0) return TD_OK;
+  return launch_adaln(a, stream);
 }
 
 int td_cache_append(const td_append_args *p, td_stream_t stream) {

@@ -58,6 +58,7 @@ int validate_commit(const td_commit_args *c, bool check_ptrs);
 int validate_append(const td_append_args *p);
 int validate_lmhead(const td_lmhead_args *a, bool check_ptrs);
 int validate_mamba(const td_mamba_args *a);
+int validate_adaln(const td_adaln_args *a);
 AttnPlan plan_attn(const td_attn_args *a);
 CommitPlan plan_commit(const td_commit_args *c);
 
@@ -88,5 +89,6 @@ inline size_t lmhead_ws_bytes(const td_lmhead_args *a) {
 }
 int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream);
 int launch_mamba(const td_mamba_args *a, void *stream);
+int launch_adaln(const td_adaln_args *a, void *stream);
 
 }  // namespace td

@@ -97,6 +97,36 @@ int validate_append(const td_append_args *p) {
   return TD_OK;
 }
 
+int validate_adaln(const td_adaln_args *a) {
+  if (!a) return TD_ERR_INVALID;
+  if (a->B < 0 || a->S < 0 || a->H < 1) return TD_ERR_INVALID;
+  if (!finite_f(a->eps) || a->eps < 0.f) return TD_ERR_INVALID;
+  if (a->H % 8 != 0 || a->H > 8192) return TD_ERR_UNSUPPORTED;
+  const int64_t M = int64_t(a->B) * a->S;
+  if (M > (int64_t(1) << 30)) return TD_ERR_UNSUPPORTED;
+  if (M == 0) return TD_OK;
+  if (!a->x || !a->t_mod || !a->h || (a->f && !a->r_out)) return TD_ERR_INVALID;
+  const void *r_out = a->f ? a->r_out : nullptr;     // unused without f
+  for (const void *q : {a->x, a->f, (const void *)a->t_mod, (const void *)a->tab_gate,
+                        (const void *)a->tab_shift, (const void *)a->tab_scale,
+                        (const void *)a->w_norm, r_out, (const void *)a->h})
+    if (!aligned16(q)) return TD_ERR_INVALID;
+  const int64_t act = M * a->H * 2, row = int64_t(a->H) * 4;
+  const Range ins[] = {range(a->x, act), range(a->f, act), range(a->t_mod, int64_t(a->B) * 3 * row),
+                       range(a->tab_gate, row), range(a->tab_shift, row), range(a->tab_scale, row),
+                       range(a->w_norm, row)};
+  const Range outs[] = {range(r_out, act), range(a->h, act)};
+  // r_out may be x itself, h may be x or f itself (each row is read whole
+  // before any of it is written); any other overlap with an input is refused
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(outs[0], ins[i]) && !(i == 0 && r_out == a->x)) return TD_ERR_INVALID;
+    if (overlap(outs[1], ins[i]) && !((i == 0 && a->h == a->x) || (i == 1 && a->h == a->f)))
+      return TD_ERR_INVALID;
+  }
+  if (overlap(outs[0], outs[1])) return TD_ERR_INVALID;
+  return TD_OK;
+}
+
 int validate_lmhead(const td_lmhead_args *a, bool check_ptrs) {
   if (!a) return TD_ERR_INVALID;
   if (a->B < 1 || a->S < 1 || a->S > 64 || a->V < 1 || a->H < 1) return TD_ERR_INVALID;

@@ -227,6 +227,39 @@ typedef struct {
   void *y;                 /* out [B, S, H, P] bf16                            */
 } td_mamba_args;
 
+/*
+ * adaLN-single time conditioning between two denoiser layers (chathome,
+ * inference paragraph: the diffusion timestep modulates every layer through
+ * adaLN-single, about 1.5M parameters).  Read as PixArt-alpha's adaLN-single:
+ * a projection of the timestep shared by all layers gives each sequence three
+ * vectors (t_mod rows 0, 1, 2 = shift, scale, gate) and each layer adds its
+ * own learned [3, H] table.  Layer l's output f joins the residual stream
+ * through layer l's gate, and layer l+1 reads the RMS-normalised stream under
+ * its own shift and scale; for sequence b and token s:
+ *   r[b,s,:] = x[b,s,:] + (t_mod[b,2,:] + tab_gate) * f[b,s,:]   (x when f is NULL)
+ *   h[b,s,:] = r[b,s,:] / sqrt(mean_j r[b,s,j]^2 + eps) * w_norm
+ *                * (1 + t_mod[b,1,:] + tab_scale) + (t_mod[b,0,:] + tab_shift)
+ * Computed in fp32.  r is rounded to bf16 and h is computed from the rounded
+ * r (the stream is stored in bf16 between layers); h is rounded to bf16.
+ */
+typedef struct {
+  int32_t B;               /* sequences, >= 0                                  */
+  int32_t S;               /* tokens per sequence, >= 0                        */
+  int32_t H;               /* hidden size, a multiple of 8, 8 .. 8192          */
+  float eps;               /* RMSNorm epsilon, finite, >= 0                    */
+  const void *x;           /* [B, S, H] bf16 residual stream                   */
+  const void *f;           /* [B, S, H] bf16 output of layer l, or NULL        */
+  const float *t_mod;      /* [B, 3, H] shared timestep vectors: shift, scale, gate */
+  const float *tab_gate;   /* [H] layer l's gate row, or NULL (zeros)          */
+  const float *tab_shift;  /* [H] layer l+1's shift row, or NULL (zeros)       */
+  const float *tab_scale;  /* [H] layer l+1's scale row, or NULL (zeros)       */
+  const float *w_norm;     /* [H] layer l+1's RMSNorm weight, or NULL (ones)   */
+  void *r_out;             /* out [B, S, H] bf16 r; required when f is given,
+                              unused otherwise; may be x itself               */
+  void *h;                 /* out [B, S, H] bf16 input of layer l+1; may be x
+                              or f itself                                      */
+} td_adaln_args;
+
 /* Library identity and struct sizes, for bindings to check their layout. */
 uint32_t td_abi_version(void);
 size_t td_sizeof_attn_args(void);
@@ -234,6 +267,7 @@ size_t td_sizeof_commit_args(void);
 size_t td_sizeof_append_args(void);
 size_t td_sizeof_lmhead_args(void);
 size_t td_sizeof_mamba_args(void);
+size_t td_sizeof_adaln_args(void);
 const char *td_status_str(int status);
 
 /* Workspace each call needs, in bytes (0 when none).  Pure host functions:
@@ -286,6 +320,13 @@ int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stre
 /* Mamba-2 block scan (see td_mamba_args).  Needs no workspace.  x, Bm, Cm
  * and h0 must be 16-byte aligned, y 8-byte aligned.  Returns a td_status. */
 int td_mamba_block_scan(const td_mamba_args *a, td_stream_t stream);
+
+/* adaLN-single modulation (see td_adaln_args).  Needs no workspace.  Every
+ * pointer must be 16-byte aligned.  An output may be the same pointer as an
+ * input, as stated above, but may not otherwise overlap an input, and r_out
+ * and h may not overlap: checked on the host (TD_ERR_INVALID).  B*S = 0 is
+ * valid and enqueues nothing.  Returns a td_status. */
+int td_adaln_modulate(const td_adaln_args *a, td_stream_t stream);
 
 /* Context-cache append (see td_append_args).  Needs no workspace.  Every
  * data pointer must be 16-byte aligned; no output may overlap an input or the

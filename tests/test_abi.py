@@ -9,6 +9,7 @@ import block_diffusion_lm_td_amd as td
 from block_diffusion_lm_td_amd import _td
 
 INVALID, UNSUPPORTED, WORKSPACE = _td.TD_ERR_INVALID, _td.TD_ERR_UNSUPPORTED, _td.TD_ERR_WORKSPACE
+OK = _td.TD_OK
 FAKE = 0x10000          # a non-null pointer value; never dereferenced on these paths
 
 
@@ -32,6 +33,7 @@ def test_struct_layout_and_version(L):
     assert L.td_sizeof_append_args() == ctypes.sizeof(_td.TdAppendArgs)
     assert L.td_sizeof_lmhead_args() == ctypes.sizeof(_td.TdLmheadArgs)
     assert L.td_sizeof_mamba_args() == ctypes.sizeof(_td.TdMambaArgs)
+    assert L.td_sizeof_adaln_args() == ctypes.sizeof(_td.TdAdalnArgs)
     for rc in (0, -1, -2, -3, -4, 7):
         assert isinstance(td.status_str(rc), str)
 
@@ -268,4 +270,37 @@ def mamba(**kw):
 def test_mamba_validation(L, kw, rc):
     a = mamba(**kw)
     assert L.td_mamba_block_scan(ctypes.byref(a), None) == rc
+
+
+def adaln(**kw):
+    a = _td.TdAdalnArgs()
+    a.B, a.S, a.H, a.eps = 64, 16, 4096, 1e-5
+    (a.x, a.f, a.t_mod, a.tab_gate, a.tab_shift, a.tab_scale, a.w_norm, a.r_out,
+     a.h) = (k * GB for k in range(1, 10))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+ACT = 64 * 16 * 4096 * 2
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(B=-1), INVALID), (dict(S=-1), INVALID), (dict(H=0), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(H=12), UNSUPPORTED), (dict(H=8200), UNSUPPORTED),
+    (dict(x=None), INVALID), (dict(t_mod=None), INVALID), (dict(h=None), INVALID),
+    (dict(r_out=None), INVALID),
+    (dict(x=1 * GB + 8), INVALID), (dict(f=2 * GB + 2), INVALID), (dict(w_norm=7 * GB + 4), INVALID),
+    (dict(tab_gate=4 * GB + 8), INVALID), (dict(h=9 * GB + 8), INVALID), (dict(r_out=8 * GB + 2), INVALID),
+    # overlaps: only r_out == x, h == x and h == f are allowed
+    (dict(r_out=1 * GB + 16), INVALID), (dict(r_out=2 * GB), INVALID), (dict(h=8 * GB), INVALID),
+    (dict(h=8 * GB + ACT - 16), INVALID), (dict(h=3 * GB), INVALID), (dict(h=7 * GB - ACT + 16), INVALID),
+    (dict(r_out=1 * GB, h=1 * GB), INVALID), (dict(h=2 * GB + 16), INVALID),
+    # nothing to do: valid, nothing enqueued
+    (dict(B=0), OK), (dict(S=0), OK), (dict(B=0, x=None, h=None, t_mod=None), OK),
+])
+def test_adaln_validation(L, kw, rc):
+    a = adaln(**kw)
+    assert L.td_adaln_modulate(ctypes.byref(a), None) == rc
 

@@ -74,3 +74,10 @@ def test_algorithmic_bytes_of_the_mamba_scan():
     xy = 2 * 64 * 16 * 128 * 64 * 2                      # x in, y out (bf16)
     bc = 2 * 64 * 16 * 8 * 128 * 2                       # Bm, Cm (bf16)
     assert bench.mamba_algorithmic(w) == state + xy + bc + 64 * 16 * 128 * 4 + 2 * 128 * 4
+
+
+def test_algorithmic_bytes_of_the_adaln_modulation():
+    import synth
+    w = synth.ADALN_WORKLOADS["adaln_b64_s16_h4096"]
+    act = 64 * 16 * 4096 * 2                      # one bf16 [B, S, H] tensor
+    assert bench.adaln_algorithmic(w) == 4 * act + 64 * 3 * 4096 * 4 + 4 * 4096 * 4

@@ -400,6 +400,7 @@ def cache_append_bench(args, L):
 
 LMHEAD_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_lmhead.hip")
 LMHEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic_lmhead_bf16_b64_h4096_v131072.json")
+LMHEAD_PACKED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic_lmhead_bf16_b64_h4096_v131072_packed.json")
 
 
 def lmhead_bench(args, L):
@@ -423,6 +424,16 @@ def lmhead_bench(args, L):
     B, S, H, V = w.B, w.S, w.H, w.V
     hid = torch.from_numpy(d["hidden"].view(np.int16)).view(torch.bfloat16).to(dev)
     wh = torch.from_numpy(d["w_head"].view(np.int16)).view(torch.bfloat16).to(dev)
+    pack_us = None
+    if args.packed:
+        # the one-time rearrangement at load time, timed on its own
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wh_packed = td.td_lmhead_pack_head(wh)
+        e1.record()
+        torch.cuda.synchronize()
+        pack_us = round(e0.elapsed_time(e1) * 1e3, 1)
+        wh_row_major, wh = wh, wh_packed
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     o = dict(commit=torch.empty((B, S), dtype=torch.uint8, device=dev),
@@ -486,7 +497,7 @@ def lmhead_bench(args, L):
     c = td.commit_args(logits, o["commit"], o["token"], w.gamma, None, o["maxprob"])
     cneed = max(L.td_commit_workspace_bytes(ctypes.byref(c)), 256)
     cws = torch.empty(cneed, dtype=torch.uint8, device=dev)
-    wht = wh.t()
+    wht = (wh_row_major if args.packed else wh).t()
 
     def unfused():
         torch.matmul(hid.view(B * S, H), wht, out=logits.view(B * S, V))
@@ -508,11 +519,14 @@ def lmhead_bench(args, L):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "S": S, "H": H, "V": V, "gamma": w.gamma,
+                   "w_head": "packed (td_lmhead_pack_head, once: %s us)" % pack_us if args.packed
+                   else "row-major [V, H]",
                    "hidden_size": "assumed (not on the pages)"},
         "roofline": {"bound": "mfma", "kernel": "td_lmhead_commit (lmhead_tiles + merge + finalize)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, LMHEAD_SRC, LMHEAD_TRAFFIC_FILE),
+                     "traffic": (measured_traffic(w.name + "_packed", LMHEAD_SRC, LMHEAD_PACKED_TRAFFIC_FILE)
+                                 if args.packed else measured_traffic(w.name, LMHEAD_SRC, LMHEAD_TRAFFIC_FILE)),
                      "algorithmic_flops": B * S * flops_per_row,
                      "avg_launch_us": full["avg_launch_us"]},
         "by_eligible_fraction": {str(k): v for k, v in rows.items()},
@@ -793,6 +807,8 @@ def main():
     ap.add_argument("--lmhead", action="store_true",
                     help="time td_lmhead_commit (fused LM head + commit) instead of the step "
                          "(one JSON line)")
+    ap.add_argument("--packed", action="store_true",
+                    help="--lmhead: pass the head as td_lmhead_pack_head's packed copy")
     ap.add_argument("--fracs", default="1,0.5,0.25,0.1",
                     help="--lmhead: fractions of positions still masked to time (the first "
                          "is the headline)")

@@ -47,7 +47,7 @@ class TdLmheadArgs(ctypes.Structure):
                 ("dtype", c_int), ("gamma", c_float), ("hidden", c_void_p), ("w_head", c_void_p),
                 ("masked_in", c_void_p), ("commit", c_void_p), ("token", c_void_p),
                 ("maxprob", c_void_p), ("n_commit", c_void_p), ("masked_out", c_void_p),
-                ("tokens", c_void_p), ("n_masked_left", c_void_p)]
+                ("tokens", c_void_p), ("n_masked_left", c_void_p), ("w_head_packed", c_int32)]
 
 
 class TdMambaArgs(ctypes.Structure):
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "td_cache_append": (c_int, [P, c_void_p]),
             "td_lmhead_commit_workspace_bytes": (c_size_t, [LH]),
             "td_lmhead_commit": (c_int, [LH, c_void_p, c_size_t, c_void_p]),
+            "td_lmhead_packed_bytes": (c_size_t, [c_int32, c_int32]),
+            "td_lmhead_pack_head": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
             "td_mamba_block_scan": (c_int, [MB, c_void_p]),
             "td_adaln_modulate": (c_int, [AD, c_void_p]),
         }
@@ -229,17 +231,34 @@ def append_args(k_ctx, v_ctx, ctx_offsets, total_ctx, k_new, v_new, k_out, v_out
     return p
 
 
+class PackedHead:
+    """An LM-head weight in the packed order td_lmhead_pack_head writes
+    (a flat bf16 device tensor) with its vocabulary and hidden sizes."""
+
+    def __init__(self, data, V: int, H: int):
+        self.data, self.V, self.H = data, int(V), int(H)
+
+
 def lmhead_args(hidden, w_head, commit, token, gamma, masked_in=None, maxprob=None,
                 n_commit=None, masked_out=None, tokens=None, n_masked_left=None) -> TdLmheadArgs:
+    """w_head: the [V, H] weight, or a PackedHead."""
     torch = _torch()
     B, S, H = hidden.shape
-    V = w_head.shape[0]
     a = TdLmheadArgs()
+    if isinstance(w_head, PackedHead):
+        if w_head.H != H:
+            raise ValueError(f"packed head has H={w_head.H}, hidden has H={H}")
+        V = w_head.V
+        a.w_head = _ptr(w_head.data, "w_head", hidden.dtype, (lib().td_lmhead_packed_bytes(V, H) // 2,))
+        a.w_head_packed = 1
+    else:
+        V = w_head.shape[0]
+        a.w_head = _ptr(w_head, "w_head", hidden.dtype, (V, H))
+        a.w_head_packed = 0
     a.B, a.S, a.H, a.V = B, S, H, V
     a.dtype = _dtype_code(hidden)
     a.gamma = float(gamma)
     a.hidden = _ptr(hidden, "hidden")
-    a.w_head = _ptr(w_head, "w_head", hidden.dtype, (V, H))
     a.masked_in = _ptr(masked_in, "masked_in", torch.uint8, (B, S))
     a.commit = _ptr(commit, "commit", torch.uint8, (B, S))
     a.token = _ptr(token, "token", torch.int32, (B, S))
@@ -374,11 +393,27 @@ def td_cache_append(k_ctx, v_ctx, ctx_offsets, k_new, v_new, k_out, v_out, offse
     return k_out, v_out, offsets_out
 
 
+def td_lmhead_pack_head(w_head, *, stream=None) -> PackedHead:
+    """The [V, H] bf16 LM-head weight rearranged once for td_lmhead_commit
+    (each pipeline stage's 256 x 64 block contiguous); same results."""
+    torch = _torch()
+    L = lib()
+    V, H = w_head.shape
+    n = L.td_lmhead_packed_bytes(V, H)
+    if n == 0:
+        raise ValueError(f"td_lmhead_pack_head: unsupported V={V}, H={H}")
+    out = torch.empty(n // 2, dtype=w_head.dtype, device=w_head.device)
+    check(L.td_lmhead_pack_head(_ptr(w_head, "w_head", torch.bfloat16, (V, H)), V, H,
+                                _ptr(out, "w_packed"), _stream(stream)), "td_lmhead_pack_head")
+    return PackedHead(out, V, H)
+
+
 def td_lmhead_commit(hidden, w_head, commit, token, *, gamma, masked_in=None, maxprob=None,
                      n_commit=None, masked_out=None, tokens=None, n_masked_left=None,
                      workspace=None, stream=None):
     """Commit of one step straight from the block's hidden states [B, S, H]
-    and the LM-head weight [V, H]: the logits stay on chip."""
+    and the LM-head weight [V, H] (or its PackedHead): the logits stay on
+    chip."""
     L = lib()
     a = lmhead_args(hidden, w_head, commit, token, gamma, masked_in, maxprob, n_commit,
                     masked_out, tokens, n_masked_left)

@@ -118,6 +118,14 @@ int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stre
   return launch_lmhead(a, ws, stream);
 }
 
+size_t td_lmhead_packed_bytes(int32_t V, int32_t H) { return lmhead_packed_bytes(V, H); }
+
+int td_lmhead_pack_head(const void *w_head, int32_t V, int32_t H, void *w_packed, td_stream_t stream) {
+  const int rc = validate_lmhead_pack(w_head, V, H, w_packed);
+  if (rc != TD_OK) return rc;
+  return launch_lmhead_pack(w_head, V, H, w_packed, stream);
+}
+
 int td_mamba_block_scan(const td_mamba_args *a, td_stream_t stream) {
   const int rc = validate_mamba(a);
   if (rc != TD_OK) return rc;

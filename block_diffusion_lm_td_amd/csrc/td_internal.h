@@ -88,6 +88,9 @@ inline size_t lmhead_ws_bytes(const td_lmhead_args *a) {
   return align256(lmhead_parts_bytes(a)) + align256(M * sizeof(Part)) + (M + 1) * sizeof(int32_t);
 }
 int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream);
+size_t lmhead_packed_bytes(int32_t V, int32_t H);
+int validate_lmhead_pack(const void *w_head, int32_t V, int32_t H, const void *w_packed);
+int launch_lmhead_pack(const void *w_head, int32_t V, int32_t H, void *w_packed, void *stream);
 int launch_mamba(const td_mamba_args *a, void *stream);
 int launch_adaln(const td_adaln_args *a, void *stream);
 

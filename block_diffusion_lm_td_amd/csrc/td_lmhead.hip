@@ -148,6 +148,7 @@ __global__ __launch_bounds__(1024) void lmhead_compact(const uint8_t *__restrict
 // workgroups b with b % 8 == x) takes a contiguous range of them, its
 // workgroups in turn, so the position tiles of one head slice run at the
 // same time on one XCD and share the slice through its L2.
+template <bool kPacked>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     const bf16 *__restrict__ hidden, const bf16 *__restrict__ whead, int M, int V, int H,
     int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
@@ -172,10 +173,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
       const int i = w + kWaves * u;
       const int row = kRPI * i + lane / kCPR;
       const int c = (lane % kCPR) ^ swz(row);
-      const int rw = min(n0 + row, V - 1) - n0;
+      const int rw = min(n0 + row, V - 1) - n0;     // row-major: rows past V re-read row V-1
       const int cm = min(m0 + row, Mc - 1);
       const int rh = rows ? rows[cm] : cm;        // hidden row of this position
-      voff_w[u] = uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
+      // packed: the stage's 256 x 64 block is contiguous, rows past V are zeros
+      voff_w[u] = kPacked ? uint32_t(row) * uint32_t(kRowBytes) + uint32_t(c) * 16u
+                          : uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
       voff_h[u] = uint32_t(rh) * uint32_t(H) * 2u + uint32_t(c) * 16u;
     }
     const bf16 *wbase = whead + int64_t(n0) * H;
@@ -184,7 +187,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     const int nk = H / kTK;
     auto issue = [&](int kt) {
       const uint32_t st = lds0 + uint32_t((kt % kStages) * kStageBytes);
-      const bf16 *wb = wbase + kt * kTK, *hb = hbase + kt * kTK;
+      const bf16 *wb = kPacked ? whead + (int64_t(tn) * nk + kt) * (kTN * kTK) : wbase + kt * kTK;
+      const bf16 *hb = hbase + kt * kTK;
 #pragma unroll
       for (int u = 0; u < kIPW; ++u) {
         const uint32_t i = uint32_t(w + kWaves * u);
@@ -335,15 +339,49 @@ int launch_lmhead(const td_lmhead_args *a, void *ws, void *stream) {
     count = rows + M;
     hipLaunchKernelGGL(lmhead_compact, dim3(1), dim3(1024), 0, st, a->masked_in, M, rows, count);
   }
-  hipLaunchKernelGGL(lmhead_tiles, dim3(kGrid), dim3(kThreads), 0, st,
-                     static_cast<const bf16 *>(a->hidden), static_cast<const bf16 *>(a->w_head), M,
-                     a->V, a->H, n_tiles, rows, count, parts);
+  if (a->w_head_packed)
+    hipLaunchKernelGGL(lmhead_tiles<true>, dim3(kGrid), dim3(kThreads), 0, st,
+                       static_cast<const bf16 *>(a->hidden), static_cast<const bf16 *>(a->w_head), M,
+                       a->V, a->H, n_tiles, rows, count, parts);
+  else
+    hipLaunchKernelGGL(lmhead_tiles<false>, dim3(kGrid), dim3(kThreads), 0, st,
+                       static_cast<const bf16 *>(a->hidden), static_cast<const bf16 *>(a->w_head), M,
+                       a->V, a->H, n_tiles, rows, count, parts);
   hipLaunchKernelGGL(lmhead_merge, dim3(unsigned(M)), dim3(256), 0, st, parts, n_tiles, rows, count,
                      merged, a->n_masked_left);
   if (hipGetLastError() != hipSuccess) return TD_ERR_HIP;
   return launch_commit_finalize(merged, 1, a->B, a->S, a->gamma, a->masked_in, a->commit, a->token,
                                 a->maxprob, a->n_commit, a->masked_out, a->tokens,
                                 a->n_masked_left, stream, nullptr, a->masked_in != nullptr);
+}
+
+namespace {
+// One 16-byte chunk per thread, in the packed order: chunk d is chunk (d & 7)
+// of row (d >> 3) & 255 of block (tn, kt) = divmod(d >> 11, H / 64).  Writes
+// are contiguous; each 8 lanes read one 128-byte row segment.
+__global__ __launch_bounds__(256) void lmhead_pack(const bf16 *__restrict__ w, int V, int H,
+                                                   uint4 *__restrict__ out, int64_t chunks) {
+  const int nk = H / kTK;
+  for (int64_t d = int64_t(blockIdx.x) * 256 + threadIdx.x; d < chunks; d += int64_t(gridDim.x) * 256) {
+    const int c = int(d & 7), row = int((d >> 3) & 255);
+    const int64_t blk = d >> 11;
+    const int64_t tn = blk / nk;
+    const int kt = int(blk - tn * nk);
+    const int64_t n = tn * kTN + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n < V) v = *reinterpret_cast<const uint4 *>(w + n * H + kt * kTK + c * 8);
+    out[d] = v;
+  }
+}
+}  // namespace
+
+int launch_lmhead_pack(const void *w_head, int32_t V, int32_t H, void *w_packed, void *stream) {
+  const int64_t chunks = int64_t(lmhead_packed_bytes(V, H)) / 16;
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, int64_t(1) << 20);
+  hipLaunchKernelGGL(lmhead_pack, dim3(unsigned(blocks)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const bf16 *>(w_head), V, H,
+                     static_cast<uint4 *>(w_packed), chunks);
+  return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }
 
 }  // namespace td

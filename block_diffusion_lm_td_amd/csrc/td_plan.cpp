@@ -138,10 +138,25 @@ int validate_lmhead(const td_lmhead_args *a, bool check_ptrs) {
   const int64_t m_tiles = (M + 255) / 256, n_tiles = (int64_t(a->V) + 255) / 256;
   if (M > (1 << 24) || m_tiles * n_tiles > (int64_t(1) << 31) - 1) return TD_ERR_UNSUPPORTED;
   if (M * a->H * 2 >= (int64_t(1) << 32)) return TD_ERR_UNSUPPORTED;   // 32-bit row offsets
+  if (a->w_head_packed != 0 && a->w_head_packed != 1) return TD_ERR_INVALID;
   if (check_ptrs) {
     if (!a->hidden || !a->w_head || !a->commit || !a->token) return TD_ERR_INVALID;
     if (!aligned16(a->hidden) || !aligned16(a->w_head)) return TD_ERR_INVALID;
   }
+  return TD_OK;
+}
+
+size_t lmhead_packed_bytes(int32_t V, int32_t H) {
+  if (V < 1 || V > (1 << 30) || H < 64 || H > 65536 || H % 64 != 0) return 0;
+  return size_t((int64_t(V) + 255) / 256) * 256 * size_t(H) * 2;
+}
+
+int validate_lmhead_pack(const void *w_head, int32_t V, int32_t H, const void *w_packed) {
+  if (V < 1 || H < 1) return TD_ERR_INVALID;
+  if (lmhead_packed_bytes(V, H) == 0) return TD_ERR_UNSUPPORTED;
+  if (!w_head || !w_packed || !aligned16(w_head) || !aligned16(w_packed)) return TD_ERR_INVALID;
+  if (overlap(range(w_head, int64_t(V) * H * 2), range(w_packed, int64_t(lmhead_packed_bytes(V, H)))))
+    return TD_ERR_INVALID;
   return TD_OK;
 }
 

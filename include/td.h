@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TD_ABI_VERSION 1u
+#define TD_ABI_VERSION 2u
 
 typedef enum {
   TD_OK = 0,
@@ -186,7 +186,8 @@ typedef struct {
   td_dtype dtype;          /* TD_BF16 (TD_ERR_UNSUPPORTED otherwise)           */
   float gamma;             /* confidence threshold, finite                     */
   const void *hidden;      /* [B, S, H] final hidden state of each position    */
-  const void *w_head;      /* [V, H] LM-head weight, row j = token j            */
+  const void *w_head;      /* [V, H] LM-head weight, row j = token j, or its
+                              packed copy (w_head_packed = 1)                  */
   const uint8_t *masked_in;/* [B, S] 1 = still [MASK] (eligible); NULL = all   */
   uint8_t *commit;         /* out [B, S]                                       */
   int32_t *token;          /* out [B, S]  argmax id at every eligible position,
@@ -196,6 +197,8 @@ typedef struct {
   uint8_t *masked_out;     /* out [B, S] or NULL; may alias masked_in          */
   int32_t *tokens;         /* in/out [B, S] or NULL: ids written where committed */
   int32_t *n_masked_left;  /* out [1] or NULL                                  */
+  int32_t w_head_packed;   /* 0: w_head is [V, H] row-major; 1: w_head is the
+                              packed copy td_lmhead_pack_head wrote            */
 } td_lmhead_args;
 
 /*
@@ -316,6 +319,21 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
  * slice of the vocabulary), 16 per position and the list of eligible
  * positions.  Returns a td_status. */
 int td_lmhead_commit(const td_lmhead_args *a, void *ws, size_t ws_bytes, td_stream_t stream);
+
+/* The LM-head weight rearranged once (at load time) for td_lmhead_commit:
+ * [ceil(V/256)][H/64][256][64] bf16, i.e. for every 256-token slice of the
+ * vocabulary and every 64-wide slice of the hidden size, the 256 x 64 block
+ * td_lmhead_commit streams as one pipeline stage, stored contiguously (32 KiB);
+ * rows past V are zero.  The result is the same bit for bit as with the
+ * row-major weight, and each stage is read as one contiguous block.
+ * td_lmhead_packed_bytes returns the packed size, ceil(V/256)*256*H*2 bytes
+ * (0 for an invalid V or H).  td_lmhead_pack_head validates (H a multiple of
+ * 64, 64 .. 65536; 1 <= V <= 2^30; both pointers 16-byte aligned and not
+ * overlapping: TD_ERR_INVALID / TD_ERR_UNSUPPORTED) and enqueues the copy on
+ * `stream`.  Returns a td_status. */
+size_t td_lmhead_packed_bytes(int32_t V, int32_t H);
+int td_lmhead_pack_head(const void *w_head, int32_t V, int32_t H, void *w_packed,
+                        td_stream_t stream);
 
 /* Mamba-2 block scan (see td_mamba_args).  Needs no workspace.  x, Bm, Cm
  * and h0 must be 16-byte aligned, y 8-byte aligned.  Returns a td_status. */

@@ -27,7 +27,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_struct_layout_and_version(L):
-    assert L.td_abi_version() == 1
+    assert L.td_abi_version() == 2
     assert L.td_sizeof_attn_args() == ctypes.sizeof(_td.TdAttnArgs)
     assert L.td_sizeof_commit_args() == ctypes.sizeof(_td.TdCommitArgs)
     assert L.td_sizeof_append_args() == ctypes.sizeof(_td.TdAppendArgs)
@@ -303,4 +303,25 @@ ACT = 64 * 16 * 4096 * 2
 def test_adaln_validation(L, kw, rc):
     a = adaln(**kw)
     assert L.td_adaln_modulate(ctypes.byref(a), None) == rc
+
+
+def test_lmhead_packed_layout_validation(L):
+    assert L.td_lmhead_commit(ctypes.byref(lmhead(w_head_packed=2)), ctypes.c_void_p(FAKE),
+                              1 << 30, None) == INVALID
+    assert L.td_lmhead_packed_bytes(131072, 4096) == 131072 * 4096 * 2
+    assert L.td_lmhead_packed_bytes(257, 64) == 512 * 64 * 2
+    assert L.td_lmhead_packed_bytes(1, 128) == 256 * 128 * 2
+    for V, H in ((0, 64), (5, 100), (5, 0), (5, 32), (5, 65600), ((1 << 30) + 1, 64)):
+        assert L.td_lmhead_packed_bytes(V, H) == 0
+
+
+@pytest.mark.parametrize("w,V,H,p,rc", [
+    (GB, 0, 64, 2 * GB, INVALID), (GB, 5, 0, 2 * GB, INVALID), (GB, 5, 100, 2 * GB, UNSUPPORTED),
+    (GB, 5, 131072, 2 * GB, UNSUPPORTED), (None, 5, 64, 2 * GB, INVALID), (GB, 5, 64, None, INVALID),
+    (GB + 8, 5, 64, 2 * GB, INVALID), (GB, 5, 64, 2 * GB + 4, INVALID),
+    (GB, 300, 64, GB + 300 * 64 * 2 - 16, INVALID),       # packed copy overlaps the weight
+    (2 * GB, 300, 64, 2 * GB - 512 * 64 * 2 + 16, INVALID),
+])
+def test_lmhead_pack_validation(L, w, V, H, p, rc):
+    assert L.td_lmhead_pack_head(w, V, H, p, None) == rc
 

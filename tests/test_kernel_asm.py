@@ -37,7 +37,8 @@ def _instructions(lines):
     return [ln for ln in lines if ln and not ln.startswith(".") and not ln.endswith(":")]
 
 
-@pytest.mark.parametrize("name", ["td_attn.hip", "td_decode.hip", "td_commit.hip", "td_lmhead.hip", "td_append.hip"])
+@pytest.mark.parametrize("name", ["td_attn.hip", "td_decode.hip", "td_commit.hip", "td_lmhead.hip",
+                                  "td_append.hip", "td_mamba.hip", "td_adaln.hip"])
 def test_m0_only_feeds_the_tile_dma(name, tmp_path):
     ins = _instructions(_asm(name, tmp_path))
     uses = [i for i, s in enumerate(ins) if re.search(r"\bm0\b", s)]

@@ -24,10 +24,12 @@ pytestmark = pytest.mark.gpu
 LW = synth.LMHEAD_WORKLOADS
 
 
-def _run(d, masked, gamma, tokens_in):
+def _run(d, masked, gamma, tokens_in, packed=False):
     B, S, H = d["hidden"].shape
     hid = dev(d["hidden"], "bf16")
     wh = dev(d["w_head"], "bf16")
+    if packed:
+        wh = td.td_lmhead_pack_head(wh)
     o = dict(commit=torch.empty((B, S), dtype=torch.uint8, device="cuda"),
              token=torch.empty((B, S), dtype=torch.int32, device="cuda"),
              maxprob=torch.empty((B, S), dtype=torch.float32, device="cuda"),
@@ -50,7 +52,7 @@ def _ref(d, masked, gamma, seqs):
     return oracle.lmhead_commit(h, w, m, gamma)
 
 
-def _case(w, seed, gamma, frac=1.0, seqs=None, label=""):
+def _case(w, seed, gamma, frac=1.0, seqs=None, label="", packed=False):
     d = synth.make_lmhead_inputs(w, seed)
     B, S = w.B, w.S
     if frac >= 1.0:
@@ -59,7 +61,7 @@ def _case(w, seed, gamma, frac=1.0, seqs=None, label=""):
         masked = (np.random.default_rng([seed, 9]).random((B, S)) < frac).astype(np.uint8)
     tokens_in = np.where(masked.astype(bool), -1, 7)
     log(f"case lmhead {label or w.name}: B={B} S={S} H={w.H} V={w.V} gamma={gamma} frac={frac}")
-    g = _run(d, masked, gamma, tokens_in)
+    g = _run(d, masked, gamma, tokens_in, packed)
     seqs = list(range(B)) if seqs is None else list(seqs)
     ref = _ref(d, masked, gamma, seqs)
     # positions already committed are not scored: token -1, maxprob 0; the
@@ -146,3 +148,52 @@ def test_lmhead_realistic_sampled():
     assert (np.abs(g["maxprob"][seqs].reshape(-1) - p) <= tol).all(), "maxprob outside the bound"
     log(f"[lmhead] realistic: E_m median {np.median(E):.2e}, max {E.max():.2e}; "
         f"positions near a tie {int((~sure).sum())} of {len(sure)}")
+
+
+def _packed_ref(w, V, H):
+    """The packed order written with plain reshapes: rows padded with zeros to
+    a multiple of 256, then [V/256][256][H/64][64] -> [V/256][H/64][256][64]."""
+    nt = (V + 255) // 256
+    p = torch.zeros((nt * 256, H), dtype=w.dtype, device=w.device)
+    p[:V] = w
+    return p.reshape(nt, 256, H // 64, 64).permute(0, 2, 1, 3).contiguous().reshape(-1)
+
+
+@pytest.mark.parametrize("V,H", [(1, 64), (255, 128), (256, 64), (257, 64), (2049, 512), (5000, 256),
+                                 (131072, 4096)])
+def test_lmhead_pack_head_layout(V, H):
+    """Every bit of the packed copy, for arbitrary bit patterns (NaN and
+    infinity payloads included)."""
+    log(f"case lmhead pack V={V} H={H}")
+    g = torch.Generator(device="cuda").manual_seed(V + H)
+    bits = torch.randint(-32768, 32768, (V, H), dtype=torch.int32, device="cuda", generator=g)
+    w = bits.to(torch.int16).view(torch.bfloat16)
+    p = td.td_lmhead_pack_head(w)
+    assert (p.V, p.H) == (V, H)
+    assert torch.equal(p.data.view(torch.int16), _packed_ref(w, V, H).view(torch.int16))
+
+
+@pytest.mark.parametrize("B,S,H,V", [
+    (20, 16, 192, 300), (1, 16, 64, 256), (3, 64, 128, 1), (2, 1, 64, 7), (9, 32, 512, 2049),
+])
+def test_lmhead_packed_exact_shapes(B, S, H, V):
+    """The packed head against the oracle on the exact grids."""
+    w = LW["lmhead_exact_b4_h256_v5000"].with_(B=B, S=S, H=H, V=V)
+    _case(w, 62 + B + H, 0.8, 0.75, label=f"packed exact B{B} S{S} H{H} V{V}", packed=True)
+
+
+@pytest.mark.parametrize("frac", [1.0, 0.3])
+def test_lmhead_packed_equals_row_major_full_step(frac):
+    """The batched step's 4096 x 131072 head, realistic values: the packed
+    head gives the row-major head's outputs bit for bit (same products, same
+    order)."""
+    w = LW["lmhead_bf16_b64_h4096_v131072"]
+    d = synth.make_lmhead_inputs(w, 67)
+    masked = (np.random.default_rng(68).random((w.B, w.S)) < frac).astype(np.uint8)
+    tokens_in = np.where(masked.astype(bool), -1, 7)
+    log(f"case lmhead packed vs row-major b64 h4096 v131072 frac={frac}")
+    a = _run(d, masked, 0.8, tokens_in)
+    b = _run(d, masked, 0.8, tokens_in, packed=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+

@@ -2,6 +2,7 @@
 include/td.h declares, its structs match the binding, and invalid arguments
 are rejected on the host before anything is enqueued (no compute calls)."""
 import ctypes
+import os
 
 import pytest
 
@@ -325,3 +326,29 @@ def test_lmhead_packed_layout_validation(L):
 def test_lmhead_pack_validation(L, w, V, H, p, rc):
     assert L.td_lmhead_pack_head(w, V, H, p, None) == rc
 
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No CPU fallback: with libtd.so absent every entry raises before doing
+    anything."""
+    monkeypatch.setattr(_td, "LIB_PATH", str(tmp_path / "libtd.so"))
+    monkeypatch.setattr(_td, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _td.lib()
+    for call in (lambda: td.td_adaln_modulate(None, None, None, None),
+                 lambda: td.td_mamba_block_scan(*([None] * 8)),
+                 lambda: td.td_cache_append(*([None] * 8), total_ctx=0)):
+        with pytest.raises(RuntimeError, match="not built"):
+            call()
+
+
+def test_product_package_never_imports_the_oracle():
+    """The oracle is test infrastructure: nothing under the package imports
+    it (or the input generators)."""
+    import re
+    pkg = os.path.dirname(_td.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(root, f), errors="replace").read()
+                assert not re.search(r"^\s*(import|from)\s+(oracle|synth)\b", txt, re.M), f

@@ -27,6 +27,7 @@ METRIC = "denoise steps/sec (S=16, ctx 8K, B=64) and % of HBM/MFMA roofline, 1 G
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 ATTN_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_attn.hip")
+DECODE_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_bf16_b64_ragged1k_8k.json")
 APPEND_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_append.hip")
 APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_traffic_bf16_b64_ragged1k_8k.json")
@@ -965,7 +966,10 @@ def main():
 
     attn_bytes, attn_flops, commit_bytes = algorithmic(w, a["lengths"])
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    # decode-shaped blocks run attn_decode (the same rule as the library's plan)
+    decode = w.dtype == "bf16" and w.D == 128 and w.G * w.S <= 16 and w.B <= 4096
+    traffic = measured_traffic(w.name, DECODE_SRC if decode else ATTN_SRC,
+                               os.path.join(ROOT, "profiles", f"attn_traffic_{w.name}.json"))
     steps_per_s = 1e3 / ms_per_step
     res = {
         "metric": METRIC,
@@ -987,8 +991,7 @@ def main():
         "tokens_per_s": round(committed * steps_per_s, 1),
         "committed_per_step": committed,
         "roofline": {"bound": "hbm", "kernel": "td_block_attn (attn_decode + decode_merge)"
-                     if w.dtype == "bf16" and w.D == 128 and w.G * w.S <= 16 and w.B <= 4096
-                     else "td_block_attn (attn_bf16_mfma + attn_merge)",
+                     if decode else "td_block_attn (attn_bf16_mfma + attn_merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": attn_bytes, "avg_launch_us": round(attn_ms * 1e3, 2),

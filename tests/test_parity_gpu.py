@@ -456,3 +456,76 @@ def test_block_loop_device_resident(S):
     assert torch.equal(g["tokens"], tokens_h) and torch.equal(g["masked"], masked_h)
     assert bool((g["tokens"] >= 0).all())
     log(f"[device loop] S={S}: {n} steps of {S} enqueued")
+
+
+def test_block_loop_graph_replay():
+    """The device-resident loop (S gated steps, no host round trip) captured
+    once in a graph and replayed three times, with eager resets and
+    synchronisations between the replays: every replay gives exactly the
+    host-driven loop's counts, tokens and masks.  The library records kernel
+    launches only (no memset nodes)."""
+    S, gamma = 16, 0.8
+    w, a, d, logits, peak, stored = _loop_setup(S, gamma, 6300)
+    B = w.B
+    rows = torch.arange(B * S, device="cuda")
+    aa = td.attn_args(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["offsets"],
+                      torch.empty_like(d["q"]), a["total_ctx"], a["max_ctx"])
+    log("case graph-replayed loop: host-driven reference")
+    h = _commit_bufs(B, S)
+    n_h = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ch = _cargs(logits, h, gamma, n_h)
+    left_h = []
+    while True:
+        logits.view(-1, w.V)[rows, peak] = stored[len(left_h)]
+        td.td_denoise_step(aa, ch)
+        left_h.append(int(n_h.item()))
+        if left_h[-1] == 0:
+            break
+        assert len(left_h) < S, "block did not finish within S steps"
+    n = len(left_h)
+
+    g = _commit_bufs(B, S)
+    cnt = torch.zeros((2,), dtype=torch.int32, device="cuda")
+    cg = [_cargs(logits, g, gamma, cnt[k:k + 1]) for k in range(2)]
+    hist = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+    ws = td.Workspace(torch.device("cuda"))
+
+    def reset():
+        for k in ("commit", "token", "maxprob", "n_commit"):
+            g[k].zero_()
+        g["masked"].fill_(1)
+        g["tokens"].fill_(-1)
+        cnt.zero_()
+        cnt[1] = 1                                    # opens step 0
+        hist.fill_(-1)
+
+    def loop():
+        for k in range(S):
+            logits.view(-1, w.V)[rows, peak] = stored[k]
+            td.td_denoise_step_if(aa, cg[k % 2], cnt[(k + 1) % 2:(k + 1) % 2 + 1], workspace=ws)
+            hist[k:k + 1].copy_(cnt[k % 2:k % 2 + 1])
+
+    def check(label):
+        got = hist.cpu().numpy().tolist()
+        assert got[:n] == left_h and all(x == 0 for x in got[n:]), (label, got, left_h)
+        assert torch.equal(g["tokens"], h["tokens"]) and torch.equal(g["masked"], h["masked"]), label
+
+    log("case graph-replayed loop: eager warm-up")
+    reset()
+    loop()                                            # allocates the workspace outside the capture
+    torch.cuda.synchronize()
+    check("eager")
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    log("case graph-replayed loop: capture")
+    with torch.cuda.graph(graph):
+        loop()
+    for rep in range(3):
+        reset()                                       # eager work between replays
+        torch.cuda.synchronize()
+        log(f"case graph-replayed loop: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        check(f"replay {rep}")
+    log(f"[graph loop] {n} steps of {S}, 3 replays identical to the host-driven loop")

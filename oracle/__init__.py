@@ -7,6 +7,7 @@ from .td_oracle import (  # noqa: F401
     block_attention,
     row_confidence,
     confidence_commit,
+    commit_decision,
     denoise_step,
     denoise_loop,
     cache_append,

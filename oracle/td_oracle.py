@@ -113,12 +113,25 @@ def confidence_commit(logits, eligible, gamma):
     Returns dict(commit bool [B,S], token int64 [B,S], maxprob float64 [B,S],
                  n_commit int64 [B]).
 
+    The confidence of every position (row_confidence), then the decision
+    (commit_decision).
+    """
+    p, token = row_confidence(logits)
+    return commit_decision(p, token, eligible, gamma)
+
+
+def commit_decision(p, token, eligible, gamma):
+    """The block decision of one step from every position's confidence p
+    [B, S] and argmax token [B, S] (as row_confidence returns them).
+
     C_b = {i eligible : p_i >= gamma}; if C_b is empty while some position is
     eligible, C_b = {the eligible i of largest p_i, lowest i on ties}.
     ([chathome] block-generation paragraph: several tokens may commit per
     step, and every block finishes; evaluation paragraph: threshold gamma.)
+    Returns the same dict as confidence_commit.
     """
-    p, token = row_confidence(logits)
+    p = np.asarray(p, dtype=np.float64)
+    token = np.asarray(token, dtype=np.int64)
     B, S = p.shape
     elig = np.ones((B, S), dtype=bool) if eligible is None else np.asarray(eligible).astype(bool)
     g = float(np.float32(gamma))

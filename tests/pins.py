@@ -441,8 +441,26 @@ def pin_step_masks(step):
     assert r["n_masked_left"] == int(mo.sum())
 
 
+def pin_step_attention_sdpa(step):
+    """The step's attention output is the layer's block attention: per
+    sequence, torch SDPA (float64, GQA) over [context ; block] keys, with the
+    default scale and with an explicit one ([chathome] inference paragraph).
+    Block and context K/V are all distinct draws, so a swapped or dropped
+    operand in the step's wiring changes the output."""
+    rng = np.random.default_rng(45)
+    a = rand_attn(rng, 3, 4, 4, 2, 8, [5, 0, 3])
+    x = rng.standard_normal((3, 4, 7)) * 2
+    m_in = np.ones((3, 4), np.uint8)
+    tok_in = np.full((3, 4), -1)
+    for scale in (None, 0.3):
+        r = step(a, x, m_in, tok_in, 0.8, scale)
+        out = np.asarray(r["out"])
+        for b in range(3):
+            _close(out[b], sdpa_seq(a, b, scale=scale), what=f"step out b={b} scale={scale}")
+
+
 LOOP_PINS = [pin_loop_force_one_is_ar, pin_loop_low_gamma_one_step, pin_loop_steps_monotone]
-STEP_PINS = [pin_step_masks]
+STEP_PINS = [pin_step_masks, pin_step_attention_sdpa]
 
 
 # ----------------------------------------------------------------------------

@@ -72,6 +72,12 @@ MUTANTS = [
     ("adaln_table_ignored", "shift = t_mod[:, 0, :] + row(tab_shift, 0.0)", "shift = t_mod[:, 0, :]"),
     ("adaln_norm_of_x", "rms = np.sqrt(np.mean(r * r, axis=2", "rms = np.sqrt(np.mean(x * x, axis=2"),
     ("adaln_norm_over_tokens", "np.mean(r * r, axis=2, keepdims=True)", "np.mean(r * r, axis=(1, 2), keepdims=True)"),
+    ("step_swaps_block_kv", 'out = block_attention(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"],',
+     'out = block_attention(a["q"], a["v_blk"], a["k_blk"], a["k_ctx"], a["v_ctx"],'),
+    ("step_swaps_context_kv", 'out = block_attention(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"],',
+     'out = block_attention(a["q"], a["k_blk"], a["v_blk"], a["v_ctx"], a["k_ctx"],'),
+    ("step_drops_scale", '                          a["offsets"], scale)\n    c = confidence_commit',
+     '                          a["offsets"], None)\n    c = confidence_commit'),
     ("append_new_rows_truncated", "k_ctx[start:stop], k_new[b]]", "k_ctx[start:stop], k_new[b, 1:]]"),
 ]
 

@@ -413,8 +413,9 @@ def test_denoise_step_if_gate_zero_and_one():
 def test_block_loop_device_resident(S):
     """S gated steps enqueued back to back, the gate of each step being the
     previous step's n_masked_left (two counters used alternately), with one
-    synchronisation at the end, give exactly the host-driven loop's result
-    (which test_block_loop_teacher_forced checks against the oracle)."""
+    synchronisation at the end, give exactly the host-driven loop's result.
+    The gated loop itself is compared step by step with the oracle at the
+    loop workload's full shape in test_loop_gpu.py."""
     gamma = 0.8
     w, a, d, logits, peak, stored = _loop_setup(S, gamma, 6200 + S)
     B = w.B
@@ -463,7 +464,8 @@ def test_block_loop_graph_replay():
     once in a graph and replayed three times, with eager resets and
     synchronisations between the replays: every replay gives exactly the
     host-driven loop's counts, tokens and masks.  The library records kernel
-    launches only (no memset nodes)."""
+    launches only (no memset nodes).  test_loop_gpu.py compares graph-replayed
+    loops with the oracle step by step at the loop workload's full shape."""
     S, gamma = 16, 0.8
     w, a, d, logits, peak, stored = _loop_setup(S, gamma, 6300)
     B = w.B

@@ -31,6 +31,8 @@ DECODE_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_decode.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_bf16_b64_ragged1k_8k.json")
 APPEND_SRC = os.path.join(ROOT, "block_diffusion_lm_td_amd", "csrc", "td_append.hip")
 APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_traffic_bf16_b64_ragged1k_8k.json")
+PART_WARMUP = 10        # untimed launches of one part before it is timed on its own
+PART_LAUNCHES = 100     # at least this many launches of one part are timed back to back
 
 
 def log(*a):
@@ -937,20 +939,30 @@ def main():
     ms_per_step = total_ms / args.steps
     log(f"[bench] {args.steps} steps in {total_ms:.3f} ms -> {ms_per_step * 1e3:.1f} us/step")
 
-    # ---- per-kernel durations: HIP events around each part on the launch stream
-    ra_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
-    for i in range(args.steps):
-        aa_ref, cc_ref = refs[i % nsets]
-        ra_ev[3 * i].record(stream)
-        r1 = L.td_block_attn(aa_ref, ws_ptr, ws.numel(), sp)
-        ra_ev[3 * i + 1].record(stream)
-        r2 = L.td_commit(cc_ref, ws_ptr, ws.numel(), sp)
-        ra_ev[3 * i + 2].record(stream)
-        if r1 or r2:
-            raise RuntimeError(_td.status_str(r1 or r2))
-    torch.cuda.synchronize()
-    attn_ms = float(np.mean([ra_ev[3 * i].elapsed_time(ra_ev[3 * i + 1]) for i in range(args.steps)]))
-    commit_ms = float(np.mean([ra_ev[3 * i + 1].elapsed_time(ra_ev[3 * i + 2]) for i in range(args.steps)]))
+    # ---- per-part durations: each part on its own, after its own warm-up,
+    # PART_LAUNCHES launches back to back between one pair of HIP events on
+    # the launch stream (the average launch duration, as a kernel trace
+    # reports it, plus the small gap between consecutive launches)
+    def part_ms(call):
+        for i in range(PART_WARMUP):
+            call(refs[i % nsets])
+        n = max(PART_LAUNCHES, args.steps)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            r = call(refs[i % nsets])
+            if r != 0:
+                raise RuntimeError(_td.status_str(r))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    attn_ms = part_ms(lambda r: L.td_block_attn(r[0], ws_ptr, ws.numel(), sp))
+    commit_ms = part_ms(lambda r: L.td_commit(r[1], ws_ptr, ws.numel(), sp))
+    log(f"[bench] td_block_attn {attn_ms * 1e3:.1f} us, td_commit {commit_ms * 1e3:.1f} us "
+        f"(back to back, after {PART_WARMUP} warm-up launches each)")
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

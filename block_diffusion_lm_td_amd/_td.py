@@ -163,10 +163,13 @@ def _ptr(t, name, dtype=None, shape=None):
     return t.data_ptr()
 
 
-def _stream(stream):
+def _torch_stream(stream, device=None):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _stream(stream):
+    return c_void_p(_torch_stream(stream).cuda_stream)
 
 
 def attn_args(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, total_ctx, max_ctx,
@@ -307,28 +310,39 @@ def adaln_args(x, f, t_mod, h, r_out=None, *, tab_gate=None, tab_shift=None, tab
 
 class Workspace:
     """Caller-owned device scratch for the td_* calls (a torch byte tensor,
-    grown on demand; torch's allocator returns 256-byte aligned blocks)."""
+    grown on demand; torch's allocator returns 256-byte aligned blocks).
+
+    A call's kernels use the buffer until they finish on the call's stream.
+    One Workspace must therefore not serve two calls that may run at the same
+    time on different streams (their partials would race); calls in order on
+    one stream may share it.  Every use records its stream on the buffer, so
+    that a buffer replaced when it grows is not handed out again by torch's
+    allocator before the kernels already enqueued on those streams are done."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, stream=None):
         torch = _torch()
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        if stream is not None and not torch.cuda.is_current_stream_capturing():
+            self.buf.record_stream(stream)
         return c_void_p(self.buf.data_ptr()), self.buf.numel()
 
 
 _default_ws = {}
 
 
-def _ws(workspace, device):
+def _ws(workspace, device, stream):
+    """The caller's workspace, else a default one per (device, stream): calls
+    on different streams never share a default workspace."""
     if workspace is not None:
         return workspace
-    key = str(device)
+    key = (str(device), int(stream.cuda_stream))
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
@@ -342,8 +356,9 @@ def td_block_attn(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, *, total_ctx,
     L = lib()
     a = attn_args(q, k_blk, v_blk, k_ctx, v_ctx, ctx_offsets, out, total_ctx, max_ctx, scale)
     need = L.td_attn_workspace_bytes(ctypes.byref(a))
-    ptr, n = _ws(workspace, q.device).get(need)
-    check(L.td_block_attn(ctypes.byref(a), ptr, n, _stream(stream)), "td_block_attn")
+    ts = _torch_stream(stream, q.device)
+    ptr, n = _ws(workspace, q.device, ts).get(need, ts)
+    check(L.td_block_attn(ctypes.byref(a), ptr, n, c_void_p(ts.cuda_stream)), "td_block_attn")
     return out
 
 
@@ -353,8 +368,9 @@ def td_commit(logits, commit, token, *, gamma, masked_in=None, maxprob=None, n_c
     c = commit_args(logits, commit, token, gamma, masked_in, maxprob, n_commit, masked_out,
                     tokens, n_masked_left)
     need = L.td_commit_workspace_bytes(ctypes.byref(c))
-    ptr, n = _ws(workspace, logits.device).get(need)
-    check(L.td_commit(ctypes.byref(c), ptr, n, _stream(stream)), "td_commit")
+    ts = _torch_stream(stream, logits.device)
+    ptr, n = _ws(workspace, logits.device, ts).get(need, ts)
+    check(L.td_commit(ctypes.byref(c), ptr, n, c_void_p(ts.cuda_stream)), "td_commit")
 
 
 def td_denoise_step(attn: TdAttnArgs, commit: TdCommitArgs, *, workspace=None, device=None,
@@ -363,9 +379,10 @@ def td_denoise_step(attn: TdAttnArgs, commit: TdCommitArgs, *, workspace=None, d
     commit_args): block attention, then the commit, on one stream."""
     L = lib()
     need = L.td_denoise_workspace_bytes(ctypes.byref(attn), ctypes.byref(commit))
-    ptr, n = _ws(workspace, device).get(need)
-    check(L.td_denoise_step(ctypes.byref(attn), ctypes.byref(commit), ptr, n, _stream(stream)),
-          "td_denoise_step")
+    ts = _torch_stream(stream, device)
+    ptr, n = _ws(workspace, device, ts).get(need, ts)
+    check(L.td_denoise_step(ctypes.byref(attn), ctypes.byref(commit), ptr, n,
+                            c_void_p(ts.cuda_stream)), "td_denoise_step")
 
 
 def td_denoise_step_if(attn: TdAttnArgs, commit: TdCommitArgs, gate, *, workspace=None,
@@ -377,9 +394,10 @@ def td_denoise_step_if(attn: TdAttnArgs, commit: TdCommitArgs, gate, *, workspac
     L = lib()
     g = _ptr(gate, "gate", torch.int32, (1,))
     need = L.td_denoise_workspace_bytes(ctypes.byref(attn), ctypes.byref(commit))
-    ptr, n = _ws(workspace, device).get(need)
+    ts = _torch_stream(stream, device)
+    ptr, n = _ws(workspace, device, ts).get(need, ts)
     check(L.td_denoise_step_if(ctypes.byref(attn), ctypes.byref(commit), c_void_p(g), ptr, n,
-                               _stream(stream)), "td_denoise_step_if")
+                               c_void_p(ts.cuda_stream)), "td_denoise_step_if")
 
 
 def td_cache_append(k_ctx, v_ctx, ctx_offsets, k_new, v_new, k_out, v_out, offsets_out, *,
@@ -418,8 +436,9 @@ def td_lmhead_commit(hidden, w_head, commit, token, *, gamma, masked_in=None, ma
     a = lmhead_args(hidden, w_head, commit, token, gamma, masked_in, maxprob, n_commit,
                     masked_out, tokens, n_masked_left)
     need = L.td_lmhead_commit_workspace_bytes(ctypes.byref(a))
-    ptr, n = _ws(workspace, hidden.device).get(need)
-    check(L.td_lmhead_commit(ctypes.byref(a), ptr, n, _stream(stream)), "td_lmhead_commit")
+    ts = _torch_stream(stream, hidden.device)
+    ptr, n = _ws(workspace, hidden.device, ts).get(need, ts)
+    check(L.td_lmhead_commit(ctypes.byref(a), ptr, n, c_void_p(ts.cuda_stream)), "td_lmhead_commit")
 
 
 def td_mamba_block_scan(x, dt, A, Bm, Cm, D, h0, y, *, stream=None):

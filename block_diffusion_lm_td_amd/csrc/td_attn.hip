@@ -25,8 +25,9 @@
 // max altogether: P is computed against the running max and the max is only
 // taken (and O rescaled) when a lane's sum of P exceeds 256.
 //
-// Any other dtype / head dim: attn_valu, one thread per query row (a plain
-// correctness path for small fp32 problems).
+// fp32 (D = 64 or 128): attn_valu, one thread per query row (a plain
+// correctness path for small problems).  bf16 with another head dim is
+// rejected on the host.
 #include <hip/hip_runtime.h>
 
 #include "td_internal.h"
@@ -827,11 +828,7 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                      static_cast<const T *>(a->v_blk), static_cast<const T *>(a->k_ctx),     \
                      static_cast<const T *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx, \
                      a->S, a->Hq, a->Hkv, p.G, p.M, p.scale_log2, static_cast<T *>(a->out), gate)
-    if (a->dtype == TD_F32) {
-      if (a->D == 64) TD_VALU(float, 64); else TD_VALU(float, 128);
-    } else {
-      if (a->D == 64) TD_VALU(bf16, 64); else TD_VALU(bf16, 128);
-    }
+    if (a->D == 64) TD_VALU(float, 64); else TD_VALU(float, 128);
 #undef TD_VALU
   }
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;

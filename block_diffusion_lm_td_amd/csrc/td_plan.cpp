@@ -21,6 +21,8 @@ int validate_attn(const td_attn_args *a, bool check_ptrs) {
   if (a->Hq / a->Hkv > 64) return TD_ERR_UNSUPPORTED;
   if (a->dtype != TD_F32 && a->dtype != TD_BF16) return TD_ERR_INVALID;
   if (a->D != 64 && a->D != 128) return TD_ERR_UNSUPPORTED;
+  // bf16 runs on the MFMA kernels, which are built for D = 128 only
+  if (a->dtype == TD_BF16 && a->D != 128) return TD_ERR_UNSUPPORTED;
   if (!(a->scale == a->scale) || isinf(a->scale)) return TD_ERR_INVALID;
   if (a->total_ctx < 0 || a->max_ctx < 0 || a->max_ctx > a->total_ctx) return TD_ERR_INVALID;
   if (a->max_ctx > (int64_t(1) << 30)) return TD_ERR_UNSUPPORTED;

@@ -84,7 +84,10 @@ typedef struct {
   int32_t B;               /* sequences (blocks) in the batch, >= 1            */
   int32_t S;               /* block size, 1 .. 64                              */
   int32_t Hq, Hkv;         /* query / KV heads, Hq % Hkv == 0, Hq/Hkv <= 64    */
-  int32_t D;               /* head dim: 64 or 128 (bf16 requires 128)          */
+  int32_t D;               /* head dim.  bf16: 128 (the MFMA kernels).  fp32:
+                              64 or 128, on a plain one-thread-per-query-row
+                              kernel meant for small problems.  Any other
+                              value: TD_ERR_UNSUPPORTED                      */
   td_dtype dtype;          /* dtype of q, k_*, v_*, out (one per call)         */
   float scale;             /* softmax scale; <= 0 selects 1/sqrt(D)            */
   const void *q;           /* [B, S, Hq, D]                                    */

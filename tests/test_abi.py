@@ -62,7 +62,7 @@ def commit(**kw):
 @pytest.mark.parametrize("kw,rc", [
     (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(S=65), INVALID),
     (dict(Hq=30, Hkv=4), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID),
-    (dict(D=96), UNSUPPORTED), (dict(dtype=7), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(D=64), UNSUPPORTED), (dict(dtype=7), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(total_ctx=-1), INVALID), (dict(max_ctx=4000), INVALID),
     (dict(total_ctx=5000, max_ctx=2000), INVALID),
     (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(ctx_offsets=None), INVALID),

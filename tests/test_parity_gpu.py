@@ -37,7 +37,7 @@ def test_attn_tiny_f32():
     check_attn(got, oracle_attn(a), "tiny_f32", fp32=True)
 
 
-@pytest.mark.parametrize("D,dtype", [(128, "f32"), (64, "bf16")])
+@pytest.mark.parametrize("D,dtype", [(128, "f32"), (64, "f32")])
 def test_attn_valu_path_other_shapes(D, dtype):
     w = W["tiny_f32_b1_ctx64"].with_(B=3, D=D, dtype=dtype, Hq=6, Hkv=3, S=5)
     a = synth.make_attention_inputs(w, 7, lengths=[0, 45, 70])

@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 TD_OK, TD_ERR_INVALID, TD_ERR_UNSUPPORTED, TD_ERR_WORKSPACE, TD_ERR_HIP = 0, -1, -2, -3, -4
 TD_F32, TD_BF16 = 0, 1
+TD_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024     # td.h's TD_NOALLOC_SCRATCH_BYTES
 
 
 class TdAttnArgs(ctypes.Structure):
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "td_commit": (c_int, [C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step": (c_int, [A, C, c_void_p, c_size_t, c_void_p]),
             "td_denoise_step_if": (c_int, [A, C, c_void_p, c_void_p, c_size_t, c_void_p]),
+            "td_denoise_step_noalloc": (c_int, [A, C, c_void_p]),
             "td_cache_append": (c_int, [P, c_void_p]),
             "td_lmhead_commit_workspace_bytes": (c_size_t, [LH]),
             "td_lmhead_commit": (c_int, [LH, c_void_p, c_size_t, c_void_p]),
@@ -383,6 +385,15 @@ def td_denoise_step(attn: TdAttnArgs, commit: TdCommitArgs, *, workspace=None, d
     ptr, n = _ws(workspace, device, ts).get(need, ts)
     check(L.td_denoise_step(ctypes.byref(attn), ctypes.byref(commit), ptr, n,
                             c_void_p(ts.cuda_stream)), "td_denoise_step")
+
+
+def td_denoise_step_noalloc(attn: TdAttnArgs, commit: TdCommitArgs, *, stream=None):
+    """td_denoise_step on the library's own per-GPU scratch array: no
+    workspace, nothing allocated.  Calls that may overlap on one GPU race on
+    that array and must not be made."""
+    L = lib()
+    check(L.td_denoise_step_noalloc(ctypes.byref(attn), ctypes.byref(commit), _stream(stream)),
+          "td_denoise_step_noalloc")
 
 
 def td_denoise_step_if(attn: TdAttnArgs, commit: TdCommitArgs, gate, *, workspace=None,

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtd.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["td_attn.hip", "td_decode.hip", "td_commit.hip", "td_lmhead.hip", "td_mamba.hip", "td_adaln.hip", "td_append.hip"]
+HIP_SOURCES = ["td_attn.hip", "td_decode.hip", "td_commit.hip", "td_lmhead.hip", "td_mamba.hip", "td_adaln.hip", "td_append.hip", "td_noalloc.hip"]
 HOST_SOURCES = ["td_plan.cpp", "td_api.cpp"]
 ARCH = "gfx950"
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,7 +1,8 @@
 // extern "C" entry points of libtd.so (declared and documented in td.h).
 // Validation and planning happen here, on the host, before anything is
 // enqueued; the launchers live in td_attn.hip / td_commit.hip / td_lmhead.hip /
-// td_mamba.hip / td_adaln.hip / td_append.hip.
+// td_mamba.hip / td_adaln.hip / td_append.hip, the library-held scratch of
+// td_denoise_step_noalloc in td_noalloc.hip.
 #include <stdint.h>
 
 #include "td_internal.h"
@@ -102,6 +103,21 @@ int td_commit(const td_commit_args *c, void *ws, size_t ws_bytes, td_stream_t st
 int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws, size_t ws_bytes,
                     td_stream_t stream) {
   return denoise(a, c, nullptr, ws, ws_bytes, stream);
+}
+
+int td_denoise_step_noalloc(const td_attn_args *a, const td_commit_args *c, td_stream_t stream) {
+  // validate and size first: a bad or oversized call is rejected before the
+  // scratch array is looked up
+  int rc = validate_attn(a, true);
+  if (rc != TD_OK) return rc;
+  rc = validate_commit(c, true);
+  if (rc != TD_OK) return rc;
+  if (a->B != c->B || a->S != c->S) return TD_ERR_INVALID;
+  if (td_denoise_workspace_bytes(a, c) > TD_NOALLOC_SCRATCH_BYTES) return TD_ERR_WORKSPACE;
+  void *ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc != TD_OK) return rc;
+  return denoise(a, c, nullptr, ws, TD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,

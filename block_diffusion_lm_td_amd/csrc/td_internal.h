@@ -93,5 +93,8 @@ int validate_lmhead_pack(const void *w_head, int32_t V, int32_t H, const void *w
 int launch_lmhead_pack(const void *w_head, int32_t V, int32_t H, void *w_packed, void *stream);
 int launch_mamba(const td_mamba_args *a, void *stream);
 int launch_adaln(const td_adaln_args *a, void *stream);
+// device address of the library-held scratch array on the current device
+// (td_noalloc.hip); looked up once per device, TD_ERR_HIP if that fails
+int noalloc_scratch(void **ptr);
 
 }  // namespace td

@@ -316,6 +316,28 @@ int td_denoise_step(const td_attn_args *a, const td_commit_args *c, void *ws,
 int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
                        void *ws, size_t ws_bytes, td_stream_t stream);
 
+/* td_denoise_step with no workspace argument, for callers that cannot
+ * allocate device memory while they run: code under stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Its scratch is a
+ * library-held device array of TD_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * reserved when the library is loaded and held until the process ends; the
+ * call itself allocates and frees nothing.  Results are those of
+ * td_denoise_step with a workspace, bit for bit.
+ * Limit: a call whose td_denoise_workspace_bytes() exceeds
+ * TD_NOALLOC_SCRATCH_BYTES returns TD_ERR_WORKSPACE.  With the default
+ * launch plan, blocks of more than 16 query rows per KV head need 33 to 50
+ * MiB whatever the batch; decode-shaped blocks (at most 16 query rows per KV
+ * head) need about 4.2 KiB per 128 cached keys per KV head, so with 2 KV
+ * heads caches beyond about 1M keys in total are rejected, as is a
+ * TD_ATTN_GRID override well above the default.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different threads without ordering) race
+ * on it and must not be made.  Nothing in the array needs clearing between
+ * calls.  Otherwise as td_denoise_step: same validation and return codes;
+ * TD_ERR_HIP also if the array's device address cannot be looked up. */
+#define TD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int td_denoise_step_noalloc(const td_attn_args *a, const td_commit_args *c, td_stream_t stream);
+
 /* Fused LM head + commit (see td_lmhead_args).  hidden and w_head must be
  * 16-byte aligned, and B*S*H*2 below 2^32.  The workspace
  * (td_lmhead_commit_workspace_bytes) holds 16 bytes per (position, 256-token

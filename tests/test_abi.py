@@ -73,6 +73,31 @@ def test_attn_validation(L, kw, rc):
     assert L.td_block_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == rc
 
 
+def test_noalloc_limit_and_validation(L, monkeypatch):
+    """td_denoise_step_noalloc: the header's scratch size matches the
+    binding's; invalid arguments and calls whose workspace would exceed the
+    library-held scratch are rejected on the host, before the scratch array
+    is looked up (these run without a GPU)."""
+    import re
+    txt = open(_td.HEADER).read()
+    m = re.search(r"#define TD_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", txt)
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == _td.TD_NOALLOC_SCRATCH_BYTES
+    a, c = attn(), commit()
+    assert L.td_denoise_step_noalloc(ctypes.byref(attn(B=0)), ctypes.byref(c), None) == INVALID
+    assert L.td_denoise_step_noalloc(ctypes.byref(a), ctypes.byref(commit(B=3)), None) == INVALID
+    assert L.td_denoise_step_noalloc(ctypes.byref(attn(D=64)), ctypes.byref(c), None) == UNSUPPORTED
+    # a persistent grid of 4096 workgroups needs 2 x 4096 partial slots of 64 KiB
+    monkeypatch.setenv("TD_ATTN_GRID", "4096")
+    assert L.td_denoise_workspace_bytes(ctypes.byref(a), ctypes.byref(c)) > _td.TD_NOALLOC_SCRATCH_BYTES
+    assert L.td_denoise_step_noalloc(ctypes.byref(a), ctypes.byref(c), None) == WORKSPACE
+    monkeypatch.delenv("TD_ATTN_GRID")
+    # decode-shaped blocks over a very long packed cache: one partial per 128 keys
+    d = attn(S=1, total_ctx=1 << 27, max_ctx=1 << 26)
+    c1 = commit(S=1)
+    assert L.td_denoise_workspace_bytes(ctypes.byref(d), ctypes.byref(c1)) > _td.TD_NOALLOC_SCRATCH_BYTES
+    assert L.td_denoise_step_noalloc(ctypes.byref(d), ctypes.byref(c1), None) == WORKSPACE
+
+
 def test_attn_empty_context_needs_no_context_pointers(L):
     """total_ctx = 0: null context pointers pass validation (only the
     workspace check then stops the call, before any launch)."""

@@ -34,9 +34,19 @@ int denoise(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
   const size_t wa = align256(pa.ws_bytes), wc = align256(pc.ws_bytes);
   rc = check_ws(wa + wc, ws, ws_bytes);
   if (rc != TD_OK) return rc;
-  rc = attn_launch(a, pa, ws, stream, gate);
+  char *wsc = static_cast<char *>(ws) + wa;
+  if (pa.decode || !pa.mfma) {
+    rc = attn_launch(a, pa, ws, stream, gate);
+    if (rc != TD_OK) return rc;
+    return launch_commit(c, pc, wsc, stream, gate);
+  }
+  // MFMA path: attention main kernel, the commit's row pass, then one launch
+  // for both small tails (attention merge + commit decision)
+  rc = launch_attn(a, pa, ws, stream, gate, false);
   if (rc != TD_OK) return rc;
-  return launch_commit(c, pc, static_cast<char *>(ws) + wa, stream, gate);
+  rc = launch_commit(c, pc, wsc, stream, gate, false);
+  if (rc != TD_OK) return rc;
+  return launch_step_tail(a, pa, ws, c, pc, wsc, stream, gate);
 }
 
 }  // namespace

@@ -30,6 +30,7 @@
 // rejected on the host.
 #include <hip/hip_runtime.h>
 
+#include "td_finalize.h"
 #include "td_internal.h"
 
 namespace td {
@@ -645,14 +646,13 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
 // per (unit, 32-row block of one wave); thread (db, lane) combines the 16
 // values that lane held in fragment db, over the unit's pieces in workgroup
 // order with a running max (one pass, deterministic).
-__global__ __launch_bounds__(256) void attn_merge(
-    const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
-    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
-    const int32_t *__restrict__ gate) {
-  if (gate && *gate == 0) return;
+__device__ __forceinline__ void merge_block(
+    int64_t blk, const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M,
+    int RG, int P, const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o,
+    bf16 *__restrict__ out) {
   const int UPS = Hkv * RG;
-  const int64_t u = blockIdx.x >> 3;
-  const int w = blockIdx.x & 7;
+  const int64_t u = blk >> 3;
+  const int w = int(blk & 7);
   const int b = int(u / UPS), uis = int(u - (u / UPS) * UPS);
   const int g = uis / RG, rg = uis - (uis / RG) * RG;
   const int64_t W = prefix[B] * UPS;
@@ -719,6 +719,38 @@ __global__ __launch_bounds__(256) void attn_merge(
     *reinterpret_cast<uint2 *>(dst + gi * 8) =
         make_uint2(pack_bf16(acc[gi * 4] * inv, acc[gi * 4 + 1] * inv),
                    pack_bf16(acc[gi * 4 + 2] * inv, acc[gi * 4 + 3] * inv));
+}
+
+__global__ __launch_bounds__(256) void attn_merge(
+    const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
+    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
+    const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
+  merge_block(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+}
+
+// The tail of a denoise step in one launch: the attention merge (blocks
+// [0, merge_blocks), as attn_merge) and, beside it, the commit's block
+// decision (the remaining blocks, one wave per sequence, as
+// commit_finalize).  The two share no data; running them in one grid saves
+// a launch and its drain on the step's critical path.
+__global__ __launch_bounds__(256) void step_tail(
+    const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
+    const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
+    int64_t merge_blocks, const Part *__restrict__ parts, int R, float gamma,
+    const uint8_t *masked_in, uint8_t *__restrict__ commit, int32_t *__restrict__ token,
+    float *__restrict__ maxprob, int32_t *__restrict__ n_commit, uint8_t *masked_out,
+    int32_t *__restrict__ tokens, int32_t *__restrict__ n_masked_left,
+    const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
+  if (int64_t(blockIdx.x) < merge_blocks) {
+    merge_block(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+    return;
+  }
+  const int b = int(int64_t(blockIdx.x) - merge_blocks) * 4 + int(threadIdx.x >> 6);
+  if (b < B)
+    fin::finalize_seq(b, threadIdx.x & 63, parts, S, R, gamma, masked_in, commit, token, maxprob,
+                      n_commit, masked_out, tokens, n_masked_left, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -803,7 +835,7 @@ __global__ __launch_bounds__(64) void attn_valu(
 }  // namespace
 
 int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
-                const int32_t *gate) {
+                const int32_t *gate, bool merge) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int max_ctx = int(a->max_ctx);
   if (p.mfma) {
@@ -817,9 +849,10 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
                        a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, p.scale_log2,
                        prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out), gate);
-    hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
-                       a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
-                       static_cast<bf16 *>(a->out), gate);
+    if (merge)
+      hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
+                         a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
+                         static_cast<bf16 *>(a->out), gate);
   } else {
     dim3 grid(p.row_groups, a->Hkv, a->B);
 #define TD_VALU(T, DD)                                                                         \
@@ -831,6 +864,22 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
     if (a->D == 64) TD_VALU(float, 64); else TD_VALU(float, 128);
 #undef TD_VALU
   }
+  return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
+}
+
+int launch_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws, const td_commit_args *c,
+                     const CommitPlan &pc, void *ws_commit, void *stream, const int32_t *gate) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char *wsb = static_cast<char *>(ws);
+  const int64_t merge_blocks = p.units * 8;
+  const int64_t fin_blocks = (int64_t(c->B) + 3) / 4;
+  hipLaunchKernelGGL(step_tail, dim3(unsigned(merge_blocks + fin_blocks)), dim3(256), 0, st,
+                     reinterpret_cast<int64_t *>(wsb + p.off_prefix), a->B, a->S, a->Hq, a->Hkv, p.G,
+                     p.M, p.row_groups, p.launch, reinterpret_cast<float2 *>(wsb + p.off_ml),
+                     reinterpret_cast<bf16 *>(wsb + p.off_o), static_cast<bf16 *>(a->out),
+                     merge_blocks, static_cast<const Part *>(ws_commit), pc.R, c->gamma, c->masked_in,
+                     c->commit, c->token, c->maxprob, c->n_commit, c->masked_out, c->tokens,
+                     c->n_masked_left, gate);
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }
 

@@ -11,12 +11,15 @@
 //   work is a convert, a max, an fma, an exp2 and an add.  Lanes, waves and
 //   row parts are merged as (max, lowest index) pairs and Z rescaled to the
 //   common max, in a fixed order (deterministic).
-// commit_finalize: one wave per sequence; merges the row parts, p = 1/Z,
-//   applies p >= gamma to the eligible positions and the force-one rule
-//   (largest p among eligible, lowest position on ties), writes the outputs
-//   and counts the positions still masked.
+// commit_finalize: one wave per sequence (td_finalize.h); merges the row
+//   parts, p = 1/Z, applies p >= gamma to the eligible positions and the
+//   force-one rule (largest p among eligible, lowest position on ties),
+//   writes the outputs and counts the positions still masked.  In a denoise
+//   step the same decision runs inside the step's tail kernel instead
+//   (td_attn.hip), beside the attention merge.
 #include <hip/hip_runtime.h>
 
+#include "td_finalize.h"
 #include "td_internal.h"
 
 namespace td {
@@ -178,57 +181,8 @@ __global__ __launch_bounds__(64) void commit_finalize(
     int32_t *__restrict__ n_commit, uint8_t *masked_out, int32_t *__restrict__ tokens,
     int32_t *__restrict__ n_masked_left, const int32_t *__restrict__ gate, bool skip_inelig) {
   if (gate && *gate == 0) return;
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
-  const bool act = i < S;
-  const int64_t row = int64_t(b) * S + i;
-  float p = 0.f;
-  int idx = 0;
-  bool elig = false;
-  if (act) elig = masked_in ? masked_in[row] != 0 : true;
-  if (act && skip_inelig && !elig) {
-    idx = -1;                        // not scored: no parts were made for it
-  } else if (act) {
-    float M = kNegInf;
-    for (int r = 0; r < R; ++r) M = fmaxf(M, parts[row * R + r].m);
-    float Z = 0.f;
-    idx = kNoIndex;
-    for (int r = 0; r < R; ++r) {
-      const Part q = parts[row * R + r];
-      if (q.m == M && q.idx < idx) idx = q.idx;
-      Z += (q.m == kNegInf) ? 0.f : q.z * fast_exp2((q.m - M) * kLog2e);
-    }
-    p = 1.0f / Z;
-  }
-  const bool pass = act && elig && p >= gamma;
-  const unsigned long long pm = __ballot(pass);
-  const unsigned long long em = __ballot(act && elig);
-  bool cm = pass;
-  if (pm == 0ull && em != 0ull) {
-    float bp = (act && elig) ? p : -1.0f;
-    int bi = (act && elig) ? i : 1 << 30;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float op = __shfl_xor(bp, o);
-      const int oi = __shfl_xor(bi, o);
-      if (op > bp || (op == bp && oi < bi)) { bp = op; bi = oi; }
-    }
-    cm = act && (i == bi);
-  }
-  const unsigned long long cmask = __ballot(cm);
-  const bool still = act && elig && !cm;
-  const unsigned long long lmask = __ballot(still);
-  if (act) {
-    commit[row] = cm ? 1 : 0;
-    token[row] = idx;
-    if (maxprob) maxprob[row] = p;
-    if (masked_out) masked_out[row] = still ? 1 : 0;
-    if (tokens && cm) tokens[row] = idx;
-  }
-  if (i == 0) {
-    if (n_commit) n_commit[b] = __popcll(cmask);
-    if (n_masked_left) atomicAdd(n_masked_left, int(__popcll(lmask)));
-  }
+  fin::finalize_seq(blockIdx.x, threadIdx.x, parts, S, R, gamma, masked_in, commit, token, maxprob,
+                    n_commit, masked_out, tokens, n_masked_left, skip_inelig);
 }
 
 }  // namespace
@@ -245,7 +199,7 @@ int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,
 }
 
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
-                  const int32_t *gate) {
+                  const int32_t *gate, bool finalize) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Part *parts = reinterpret_cast<Part *>(ws);
   const unsigned nblk = unsigned(p.rows * p.R);
@@ -265,6 +219,7 @@ int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *
                          static_cast<const float *>(c->logits), c->V, p.span, p.R, parts, c->n_masked_left, gate);
   }
   if (hipGetLastError() != hipSuccess) return TD_ERR_HIP;
+  if (!finalize) return TD_OK;
   return launch_commit_finalize(parts, p.R, c->B, c->S, c->gamma, c->masked_in, c->commit, c->token,
                                 c->maxprob, c->n_commit, c->masked_out, c->tokens,
                                 c->n_masked_left, stream, gate);

@@ -67,12 +67,20 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Launchers (td_attn.hip / td_commit.hip); return a td_status.
 // gate: NULL, or a device int32 that every kernel reads first; 0 = do nothing
 // (the commit still clears n_masked_left)
+// merge = false (MFMA path only): the main kernel alone; the merge then runs in
+// launch_step_tail
 int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
-                const int32_t *gate = nullptr);
+                const int32_t *gate = nullptr, bool merge = true);
 int launch_attn_decode(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
                        const int32_t *gate = nullptr);
+// finalize = false: the row pass alone; the decision then runs in launch_step_tail
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
-                  const int32_t *gate = nullptr);
+                  const int32_t *gate = nullptr, bool finalize = true);
+// the tail of a denoise step on the MFMA attention path, in one launch: the
+// attention merge and the commit's decision (td_attn.hip); ws is the
+// attention's workspace, ws_commit the commit's
+int launch_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws, const td_commit_args *c,
+                     const CommitPlan &pc, void *ws_commit, void *stream, const int32_t *gate);
 int launch_append(const td_append_args *p, void *stream);
 // the commit's per-sequence decision over R parts per position (td_commit.hip)
 int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,

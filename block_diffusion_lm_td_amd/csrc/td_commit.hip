@@ -4,11 +4,11 @@
 // several positions may commit in one step, and every block finishes).
 //
 // commit_rows: one streaming pass over each row of logits (R workgroups per
-//   row, 16-byte loads).  Every lane keeps a running max m, the index of the
-//   first 8-element vector where it reached m, and Z = sum exp(x - m) with
-//   the usual rescale when m grows.  The argmax inside the winning vector is
-//   resolved once at the end by re-reading that vector, so the per-element
-//   work is a convert, a max, an fma, an exp2 and an add.  Lanes, waves and
+//   row, 16-byte loads).  Every lane keeps its running max, the first vector
+//   that reached it (in registers) and Z = sum exp(x - ref) against a
+//   reference max that moves only when a value exceeds it by more than e^64,
+//   so the per-element work is a convert, a max, an fma, an exp2 and an add;
+//   the argmax inside the winning vector is resolved once at the end.  Lanes, waves and
 //   row parts are merged as (max, lowest index) pairs and Z rescaled to the
 //   common max, in a fixed order (deterministic).
 // commit_finalize: one wave per sequence (td_finalize.h); merges the row
@@ -80,6 +80,64 @@ __device__ inline void absorb(const float (&f)[NV], int vi, float &m, float &z, 
   for (int k = 0; k < NV; ++k) z += fast_exp2(__builtin_fmaf(f[k], kLog2e, -mc));
 }
 
+// Vector-path lane state.  The exp sum runs against a reference max mr that
+// only moves when a value exceeds it by more than kLazyRef (exact in real
+// arithmetic; every term stays below e^kLazyRef, far from fp32 overflow even
+// summed over 2^30 logits), so the common step is a max, an fma, an exp2 and
+// an add per logit with no rescale; the vector that first reached the true
+// max mt is kept in registers, so the argmax needs no second read.
+constexpr float kLazyRef = 64.0f;
+template <typename VT>
+struct VLane {
+  float mt = -__builtin_inff();   // true running max
+  float mr = -__builtin_inff();   // reference max of the exp sum
+  float nmc = 0.f;                // -mr * log2(e) (0 while mr is -inf)
+  float z = 0.f;                  // sum of exp(x - mr)
+  int bv = -1;                    // index of the vector that first reached mt
+  VT best{};                      // that vector
+};
+
+// max of three floats in one instruction: the logits are finite or -inf, so
+// no NaN canonicalisation is needed (fmaxf would add one per value)
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <int NV>
+__device__ __forceinline__ float vec_max(const float (&f)[NV]) {
+  if constexpr (NV == 8) {
+    return max3_raw(max3_raw(f[0], f[1], f[2]), max3_raw(f[3], f[4], f[5]), max3_raw(f[6], f[7], f[7]));
+  } else {
+    float m = f[0];
+#pragma unroll
+    for (int k = 1; k < NV; ++k) m = fmaxf(m, f[k]);
+    return m;
+  }
+}
+
+template <int NV, typename VT>
+__device__ __forceinline__ void absorb_vec(const float (&f)[NV], const VT &x, int vi, VLane<VT> &s) {
+  const float vmax = vec_max<NV>(f);
+  if (vmax > s.mt) {
+    s.mt = vmax;
+    s.bv = vi;
+    s.best = x;
+  }
+  if (__any(vmax > s.mr + kLazyRef)) {
+    // rare after a row's first vectors: move the reference where it fell
+    // behind (the empty asm keeps this behind a real branch)
+    asm volatile("");
+    if (vmax > s.mr + kLazyRef) {
+      s.z *= fast_exp2((s.mr - s.mt) * kLog2e);     // mr = -inf: z is 0 and stays 0
+      s.mr = s.mt;
+      s.nmc = -s.mr * kLog2e;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NV; ++k) s.z += fast_exp2(__builtin_fmaf(f[k], kLog2e, s.nmc));
+}
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void commit_rows(const T *__restrict__ logits, int V, int span,
                                                    int R, Part *__restrict__ parts,
@@ -97,50 +155,49 @@ __global__ __launch_bounds__(256) void commit_rows(const T *__restrict__ logits,
   const int e_hi = min(V, e_lo + span);
   const T *x = logits + row * V;
 
-  float m = kNegInf, z = 0.f;
-  int bv = -1;    // vector index (VEC) or element index (scalar) of the lane's max
+  float m = kNegInf, z = 0.f;     // the lane's max and its sum of exp(x - zref)
+  float zref = kNegInf;
+  int idx = kNoIndex;              // lowest index of the lane's max
   if (VEC) {
     const VT *src = reinterpret_cast<const VT *>(x);
     const int v_lo = e_lo / NV, v_hi = e_hi / NV;
     int vi = v_lo + tid;
+    VLane<VT> s;
     for (; vi + 3 * 256 < v_hi; vi += 4 * 256) {
       const VT a0 = ldv(src + vi), a1 = ldv(src + vi + 256), a2 = ldv(src + vi + 512), a3 = ldv(src + vi + 768);
+      __builtin_amdgcn_sched_barrier(0);      // all four loads in flight before the first use
       float f[NV];
-      unpack(a0, f); absorb<NV>(f, vi, m, z, bv);
-      unpack(a1, f); absorb<NV>(f, vi + 256, m, z, bv);
-      unpack(a2, f); absorb<NV>(f, vi + 512, m, z, bv);
-      unpack(a3, f); absorb<NV>(f, vi + 768, m, z, bv);
+      unpack(a0, f); absorb_vec<NV>(f, a0, vi, s);
+      unpack(a1, f); absorb_vec<NV>(f, a1, vi + 256, s);
+      unpack(a2, f); absorb_vec<NV>(f, a2, vi + 512, s);
+      unpack(a3, f); absorb_vec<NV>(f, a3, vi + 768, s);
     }
     for (; vi < v_hi; vi += 256) {
+      const VT a = ldv(src + vi);
       float f[NV];
-      unpack(ldv(src + vi), f);
-      absorb<NV>(f, vi, m, z, bv);
+      unpack(a, f);
+      absorb_vec<NV>(f, a, vi, s);
     }
+    if (s.bv >= 0) {
+      float f[NV];
+      unpack(s.best, f);
+      int k = NV - 1;
+#pragma unroll
+      for (int kk = NV - 1; kk >= 0; --kk)
+        if (f[kk] == s.mt) k = kk;
+      idx = s.bv * NV + k;
+    }
+    m = s.mt;
+    z = s.z;
+    zref = s.mr;
   } else {
+    int bv = -1;    // element index of the lane's max
     for (int e = e_lo + tid; e < e_hi; e += 256) {
       float f[1] = {to_f(x[e])};
       absorb<1>(f, e, m, z, bv);
     }
-  }
-  // lowest index of the lane's max; only lanes holding their wave's max can
-  // hold the row's argmax, so only they re-read their best vector
-  int idx = kNoIndex;
-  float wmx = m;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wmx = fmaxf(wmx, __shfl_xor(wmx, o));
-  if (m < wmx) bv = -1;
-  if (bv >= 0) {
-    if (VEC) {
-      float f[NV];
-      unpack(reinterpret_cast<const VT *>(x)[bv], f);
-      int k = NV - 1;
-#pragma unroll
-      for (int kk = NV - 1; kk >= 0; --kk)
-        if (f[kk] == m) k = kk;
-      idx = bv * NV + k;
-    } else {
-      idx = bv;
-    }
+    if (bv >= 0) idx = bv;
+    zref = m;
   }
   // wave merge of (m, idx): larger m, then lower idx
   float wm = m;
@@ -151,7 +208,7 @@ __global__ __launch_bounds__(256) void commit_rows(const T *__restrict__ logits,
     const int oi = __shfl_xor(wi, o);
     if (om > wm || (om == wm && oi < wi)) { wm = om; wi = oi; }
   }
-  float zs = (m == kNegInf) ? 0.f : z * fast_exp2((m - wm) * kLog2e);
+  float zs = (m == kNegInf) ? 0.f : z * fast_exp2((zref - wm) * kLog2e);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o);
 

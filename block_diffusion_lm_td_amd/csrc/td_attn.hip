@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int HD = 128;                 // head dim of the MFMA path
@@ -172,16 +173,26 @@ __device__ __forceinline__ void qk_half(const bf16 *__restrict__ Kt, int h, int 
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
   }
 }
+// Two P values rounded to bf16 (one v_cvt_pk_bf16_f32), stored at positions
+// i, i+1 of p, and added to the lane's row sum with one v_dot2 against
+// (1, 1): the sum is over the same rounded P the PV product uses.
+__device__ __forceinline__ float p_pair(float a, float b, bf16x8 &p, int i, float acc) {
+  const bf16x2 pr = {bf16(a), bf16(b)};
+  p[i] = pr.x;
+  p[i + 1] = pr.y;
+  const bf16x2 one = {bf16(1.0f), bf16(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+}
 // softmax of a half: P^T as bf16 (k-steps kk = 0, 1 of the half) and its lane sum
 __device__ __forceinline__ float sm_half(const f32x16 &s, float m, float sl2, bf16x8 (&p)[2]) {
   float acc = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pv = fast_exp2(__builtin_fmaf(s[kk * 8 + i], sl2, -m));
-      acc += pv;
-      p[kk][i] = bf16(pv);
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[kk * 8 + i], sl2, -m));
+      const float p1 = fast_exp2(__builtin_fmaf(s[kk * 8 + i + 1], sl2, -m));
+      acc = p_pair(p0, p1, p[kk], i, acc);
     }
   return acc;
 }
@@ -249,7 +260,7 @@ __device__ __forceinline__ float step16(const bf16 *__restrict__ Kq, int hq, con
   };
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) load(i);
-  float acc = 0.f;
+  float acc = 0.f, pe_prev = 0.f;
   sq = f32x16{};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -261,8 +272,10 @@ __device__ __forceinline__ float step16(const bf16 *__restrict__ Kq, int hq, con
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], pv[kk], o[db], 0, 0, 0);
     }
     const float pe = fast_exp2(__builtin_fmaf(ss[i], sl2, -m));
-    acc += pe;
-    ps[i >> 3][i & 7] = bf16(pe);
+    if (i & 1)
+      acc = p_pair(pe_prev, pe, ps[i >> 3], (i & 7) - 1, acc);
+    else
+      pe_prev = pe;
     if (i + kAhead < 16) load(i + kAhead);
   }
   __builtin_amdgcn_sched_barrier(0);

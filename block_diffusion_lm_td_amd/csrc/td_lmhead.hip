@@ -3,7 +3,7 @@
 // block-generation and evaluation paragraphs: every denoising step scores the
 // vocabulary at each block position, then commits by confidence).
 //
-// lmhead_tiles: logits^T = W_head . hidden^T on v_mfma_f32_32x32x16_bf16, one
+// lmhead_tiles: logits^T = W_head . hidden^T on v_mfma_f32_16x16x32_bf16, one
 //   256 (vocabulary rows) x 256 (positions) tile per workgroup, fp32
 //   accumulation.  The logits never leave the registers: the epilogue reduces
 //   each position's 256 logits of the tile to (max, lowest argmax, sum of
@@ -15,17 +15,22 @@
 //     XOR-swizzled per row so that the MFMA operand reads are free of bank
 //     conflicts.
 //   - 16 waves, four per SIMD: wave w covers head rows (w % 4)*64 .. +63 and
-//     positions (w / 4)*64 .. +63 of the tile, 2 x 2 blocks of 32 x 32.  In
-//     the transposed orientation a lane holds 16 logits of one position per
-//     block, so the reduction over the vocabulary is mostly in-lane.
+//     positions (w / 4)*64 .. +63 of the tile, 4 x 4 blocks of 16 x 16.  In
+//     the transposed orientation a lane holds 4 logits of one position per
+//     block, 16 per position over the wave's head rows, so the reduction
+//     over the vocabulary is mostly in-lane.
+//   - The 16x16x32 shape reads the same LDS bytes per flop as 32x32x16 with
+//     this 64 x 64 wave tile and the same accumulator registers, and at this
+//     chip's power limit it sustains more flops (a bare loop on random
+//     operands: 1.92 against 1.77 PF/s, at lower energy per flop).
 //   - Tiles are numbered with the position tile fastest and dealt to the
 //     XCDs in contiguous ranges, so the position tiles that share a slice of
 //     the head run together on one XCD and read it from its L2.
-//   Measured at 64 x 16 positions, H = 4096, V = 131072 (median of 5 x 10
-//   launches): this configuration 932 us; 32-wide slices in a 4-stage ring,
-//   8 waves of 64 x 128: 1154 us; 4 waves of 128 x 128: 1246 us.  Without
-//   the in-loop DMA (a timing-only copy) the same tiles take 755-792 us, the
-//   rate of the MFMA work and barriers alone at this chip's power limit.
+//   Measured at 64 x 16 positions, H = 4096, V = 131072, every position
+//   scored (median of 7 x 20 launches of td_lmhead_commit): 879 us, against
+//   927 us for the same tiles on 32x32x16 blocks.  Earlier 32x32x16 layouts:
+//   32-wide slices in a 4-stage ring, 8 waves of 64 x 128: 1154 us; 4 waves
+//   of 128 x 128: 1246 us.
 // lmhead_merge: one workgroup per position merges the tiles' partials in
 //   tile order (deterministic) into one partial, which the commit's
 //   per-sequence decision kernel then takes as a single vocabulary part.
@@ -38,7 +43,7 @@ namespace {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTM = 256;
 constexpr int kTN = 256;
@@ -56,7 +61,8 @@ constexpr int kInstr = kTN * kRowBytes / 1024; // DMA instructions per operand p
 constexpr int kIPW = kInstr / kWaves;          // per wave and operand
 constexpr int WN = 4, WM = kWaves / 4;
 constexpr int TNW = kTN / WN, TMW = kTM / WM;
-constexpr int NI = TNW / 32, NJ = TMW / 32;
+constexpr int kMB = 16;                        // v_mfma_f32_16x16x32_bf16 blocks
+constexpr int NI = TNW / kMB, NJ = TMW / kMB;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kNoIndex = 0x7fffffff;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     Part *__restrict__ parts) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
   const int wn = w % WN, wm = w / WN;
   const int Mc = count ? *count : M;
   const int m_act = (Mc + kTM - 1) / kTM;
@@ -196,11 +202,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
         dma16(hb, voff_h[u], __builtin_amdgcn_readfirstlane(st + uint32_t(kTN * kRowBytes) + i * 1024u));
       }
     };
-    f32x16 acc[NI][NJ];
+    f32x4 acc[NI][NJ];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
     for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
       const int ahead = min(kStages - 2, nk - 1 - kt);
@@ -209,27 +215,30 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
       if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
       const unsigned char *st = ring + (kt % kStages) * kStageBytes;
       const unsigned char *wl = st, *hl = st + kTN * kRowBytes;
+      // lane: row l16 of each 16-row block, hidden units ks*32 + 8*l4 .. +7
 #pragma unroll
-      for (int ks = 0; ks < kTK / 16; ++ks) {
-        const int c = ks * 2 + lh;
+      for (int ks = 0; ks < kTK / 32; ++ks) {
+        const int c = ks * 4 + l4;
         bf16x8 a[NI], bb[NJ];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int row = wn * TNW + i * 32 + lq;
+          const int row = wn * TNW + i * kMB + l16;
           a[i] = *reinterpret_cast<const bf16x8 *>(wl + row * kRowBytes + ((c ^ swz(row)) * 16));
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int row = wm * TMW + j * 32 + lq;
+          const int row = wm * TMW + j * kMB + l16;
           bb[j] = *reinterpret_cast<const bf16x8 *>(hl + row * kRowBytes + ((c ^ swz(row)) * 16));
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
     }
+    // lane: position l16 of each 16-position block, head rows 4*l4 .. +3 of
+    // each 16-row block
     float pm[NJ], pz[NJ];
     int pi[NJ];
 #pragma unroll
@@ -239,8 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int n = n0 + wn * TNW + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + wn * TNW + i * kMB + l4 * 4 + e;
           const float v = n < V ? acc[i][j][e] : kNegInf;
           acc[i][j][e] = v;
           if (v > mx) { mx = v; id = n; }
@@ -251,8 +260,9 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) z += fast_exp2(__builtin_fmaf(acc[i][j][e], kLog2e, -mc));
+          for (int e = 0; e < 4; ++e) z += fast_exp2(__builtin_fmaf(acc[i][j][e], kLog2e, -mc));
       }
+      merge_part(mx, z, id, __shfl_xor(mx, 16), __shfl_xor(z, 16), __shfl_xor(id, 16));
       merge_part(mx, z, id, __shfl_xor(mx, 32), __shfl_xor(z, 32), __shfl_xor(id, 32));
       pm[j] = mx; pz[j] = z; pi[j] = id;
     }
@@ -260,10 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     float *red_m = reinterpret_cast<float *>(ring);
     float *red_z = red_m + WN * kTM;
     int *red_i = reinterpret_cast<int *>(red_z + WN * kTM);
-    if (lh == 0) {
+    if (l4 == 0) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int p = wm * TMW + j * 32 + lq;
+        const int p = wm * TMW + j * kMB + l16;
         red_m[wn * kTM + p] = pm[j];
         red_z[wn * kTM + p] = pz[j];
         red_i[wn * kTM + p] = pi[j];

@@ -658,7 +658,11 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
 // Merge of the partials of every unit cut between workgroups: one workgroup
 // per (unit, 32-row block of one wave); thread (db, lane) combines the 16
 // values that lane held in fragment db, over the unit's pieces in workgroup
-// order with a running max (one pass, deterministic).
+// order with a running max (one pass, deterministic).  PRE pieces are
+// fetched per memory round trip: 4 keeps the registers (and the occupancy)
+// of the common case of a few pieces per unit; 16 serves long contexts,
+// whose units are cut into dozens of pieces.
+template <int PRE>
 __device__ __forceinline__ void merge_block(
     int64_t blk, const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M,
     int RG, int P, const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o,
@@ -713,7 +717,7 @@ __device__ __forceinline__ void merge_block(
   };
   // pieces are fetched kPre at a time (one memory round trip per batch) and
   // combined in workgroup order
-  constexpr int kPre = 4;
+  constexpr int kPre = PRE;
   for (int64_t base = p_first; base <= p_last; base += kPre) {
     float2 mlv[kPre];
     uint4 xa[kPre], xb[kPre];
@@ -734,12 +738,13 @@ __device__ __forceinline__ void merge_block(
                    pack_bf16(acc[gi * 4 + 2] * inv, acc[gi * 4 + 3] * inv));
 }
 
+template <int PRE>
 __global__ __launch_bounds__(256) void attn_merge(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
     const int32_t *__restrict__ gate) {
   if (gate && *gate == 0) return;
-  merge_block(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+  merge_block<PRE>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
 }
 
 // The tail of a denoise step in one launch: the attention merge (blocks
@@ -747,6 +752,7 @@ __global__ __launch_bounds__(256) void attn_merge(
 // decision (the remaining blocks, one wave per sequence, as
 // commit_finalize).  The two share no data; running them in one grid saves
 // a launch and its drain on the step's critical path.
+template <int PRE>
 __global__ __launch_bounds__(256) void step_tail(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(256) void step_tail(
     const int32_t *__restrict__ gate) {
   if (gate && *gate == 0) return;
   if (int64_t(blockIdx.x) < merge_blocks) {
-    merge_block(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+    merge_block<PRE>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
     return;
   }
   const int b = int(int64_t(blockIdx.x) - merge_blocks) * 4 + int(threadIdx.x >> 6);
@@ -845,6 +851,10 @@ __global__ __launch_bounds__(64) void attn_valu(
   for (int d = 0; d < DD; ++d) st(op + d, o[d] * inv);
 }
 
+// More than about four pieces per cut unit on average (launch workgroups
+// against units): long contexts over few sequences.
+inline bool many_pieces(const AttnPlan &p) { return int64_t(p.launch) > 4 * p.units; }
+
 }  // namespace
 
 int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
@@ -862,10 +872,12 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
                        a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, p.scale_log2,
                        prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out), gate);
-    if (merge)
-      hipLaunchKernelGGL(attn_merge, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
+    if (merge) {
+      auto k = many_pieces(p) ? attn_merge<16> : attn_merge<4>;
+      hipLaunchKernelGGL(k, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
                          a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
                          static_cast<bf16 *>(a->out), gate);
+    }
   } else {
     dim3 grid(p.row_groups, a->Hkv, a->B);
 #define TD_VALU(T, DD)                                                                         \
@@ -886,7 +898,8 @@ int launch_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws, const t
   char *wsb = static_cast<char *>(ws);
   const int64_t merge_blocks = p.units * 8;
   const int64_t fin_blocks = (int64_t(c->B) + 3) / 4;
-  hipLaunchKernelGGL(step_tail, dim3(unsigned(merge_blocks + fin_blocks)), dim3(256), 0, st,
+  auto k = many_pieces(p) ? step_tail<16> : step_tail<4>;
+  hipLaunchKernelGGL(k, dim3(unsigned(merge_blocks + fin_blocks)), dim3(256), 0, st,
                      reinterpret_cast<int64_t *>(wsb + p.off_prefix), a->B, a->S, a->Hq, a->Hkv, p.G,
                      p.M, p.row_groups, p.launch, reinterpret_cast<float2 *>(wsb + p.off_ml),
                      reinterpret_cast<bf16 *>(wsb + p.off_o), static_cast<bf16 *>(a->out),

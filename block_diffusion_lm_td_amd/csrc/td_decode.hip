@@ -247,14 +247,17 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void attn_decode(
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a01), pt, o[dt], 0, 0, 0);
     }
   };
-  // two register sets: block jb + 1 loads while block jb is processed
+  // two register sets: block jb + 1 loads while block jb is processed.  The
+  // loads are unconditional (past the piece they re-read its last key,
+  // cached): behind a branch, the compiler would wait for every load in
+  // flight, the next block's included, before using the current one.
   Blk b0, b1;
   load_blk(k0, b0);
   for (int jb = 0; jb < nblk; jb += 2) {
-    if (jb + 1 < nblk) load_blk(k0 + (jb + 1) * kBlk, b1);
+    load_blk(k0 + (jb + 1) * kBlk, b1);
     step(jb, b0);
     if (jb + 1 >= nblk) break;
-    if (jb + 2 < nblk) load_blk(k0 + (jb + 2) * kBlk, b0);
+    load_blk(k0 + (jb + 2) * kBlk, b0);
     step(jb + 1, b1);
   }
   // l: the four lanes of a query hold disjoint keys

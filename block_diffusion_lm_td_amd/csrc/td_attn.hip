@@ -114,6 +114,15 @@ __device__ inline void dma16s(const void *base, uint32_t voff, uint32_t lds_base
                : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+// The same without the non-temporal hint, for a context read by several row
+// groups: the tiles stay in L2 for the sibling workgroups (consecutive
+// logical workgroups, on one XCD) that stream the same keys at the same time.
+__device__ inline void dma16s_keep(const void *base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1\n\ts_nop 1"
+               :
+               : "s"(lds_base), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
 __device__ inline uint32_t lds_addr(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
 }
@@ -290,6 +299,9 @@ __device__ __forceinline__ void mask_half(f32x16 &s, int h, int lh, int nvalid) 
   }
 }
 
+// KEEP: units of several row groups (RG > 1) read each context tile once per
+// row group; the DMA then keeps the tiles in L2 for the siblings.
+template <bool KEEP>
 __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const bf16 *__restrict__ q, const bf16 *__restrict__ kb, const bf16 *__restrict__ vb,
     const bf16 *__restrict__ kc, const bf16 *__restrict__ vc, const int64_t *__restrict__ off,
@@ -427,10 +439,17 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
     const uint32_t lk = lds_k + uint32_t(stage) * (TE * 2), lv = lds_v + uint32_t(stage) * (TE * 2);
     if (k0 + T <= c.L) {                       // whole tile in the context cache
       const int64_t e0 = (c.lo + k0) * kvs + int64_t(g) * HD;
-      dma16s(kc + e0, dko[0], lk);
-      dma16s(vc + e0, dvo[0], lv);
-      dma16s(kc + e0, dko[1], lk + 4 * HD * 2);
-      dma16s(vc + e0, dvo[1], lv + 4 * HD * 2);
+      if (KEEP) {
+        dma16s_keep(kc + e0, dko[0], lk);
+        dma16s_keep(vc + e0, dvo[0], lv);
+        dma16s_keep(kc + e0, dko[1], lk + 4 * HD * 2);
+        dma16s_keep(vc + e0, dvo[1], lv + 4 * HD * 2);
+      } else {
+        dma16s(kc + e0, dko[0], lk);
+        dma16s(vc + e0, dvo[0], lv);
+        dma16s(kc + e0, dko[1], lk + 4 * HD * 2);
+        dma16s(vc + e0, dvo[1], lv + 4 * HD * 2);
+      }
       return;
     }
     // the tile reaches into the block's own keys (or past their end)
@@ -866,7 +885,8 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
     int64_t *prefix = reinterpret_cast<int64_t *>(wsb + p.off_prefix);
     float2 *ws_ml = reinterpret_cast<float2 *>(wsb + p.off_ml);
     bf16 *ws_o = reinterpret_cast<bf16 *>(wsb + p.off_o);
-    hipLaunchKernelGGL(attn_bf16_mfma, dim3(p.launch), dim3(kWGThreads), 0, st,
+    auto k = p.row_groups > 1 ? attn_bf16_mfma<true> : attn_bf16_mfma<false>;
+    hipLaunchKernelGGL(k, dim3(p.launch), dim3(kWGThreads), 0, st,
                        static_cast<const bf16 *>(a->q), static_cast<const bf16 *>(a->k_blk),
                        static_cast<const bf16 *>(a->v_blk), static_cast<const bf16 *>(a->k_ctx),
                        static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,

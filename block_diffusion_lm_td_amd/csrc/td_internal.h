@@ -15,7 +15,10 @@ constexpr int kKeyTile = 64;      // keys per LDS tile
 constexpr int kWaves = 8;         // 8 waves x 32 rows; two waves share each SIMD
 constexpr int kWGThreads = 64 * kWaves;
 constexpr int kGridWGs = 256;     // persistent grid: one workgroup per CU of MI355X
-constexpr int kDecodePieceKeys = 128;   // keys per wave-piece of the decode path
+constexpr int kDecodeBlockKeys = 32;    // keys per block of the decode path
+constexpr int kDecodeWaves = 4;         // waves per decode workgroup
+constexpr int kDecodeGridWGs = 512;     // one resident generation: two workgroups per CU
+constexpr int kDecodeMinBlocks = 8;     // fewer waves below about 8 blocks each
 constexpr int kDecodeMaxB = 4096;       // sequences whose piece table fits the decode kernel's LDS
 
 // Partial of the commit's vocabulary pass over one part of a row (16 bytes).
@@ -29,7 +32,7 @@ struct Part {
 // Launch plan of one td_block_attn call, derived on the host from sizes only.
 struct AttnPlan {
   bool mfma;            // bf16, D == 128: MFMA kernel; otherwise the VALU kernel
-  bool decode;          // bf16, D == 128, M <= 16: the decode kernels (units = pieces)
+  bool decode;          // bf16, D == 128, M <= 16: the decode kernels (units = partial slots)
   int G;                // Hq / Hkv
   int M;                // G * S query rows per (b, kv head)
   int row_groups;       // ceil(M / kRowsPerWG) (MFMA) or ceil(M / 64) (VALU)

@@ -176,6 +176,12 @@ int validate_mamba(const td_mamba_args *a) {
   return TD_OK;
 }
 
+static int decode_grid_override() {
+  const char *env = getenv("TD_DECODE_GRID");
+  if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);
+  return 0;
+}
+
 static int grid_override() {
   const char *env = getenv("TD_ATTN_GRID");
   if (env && atoi(env) >= 1 && atoi(env) <= 4096) return atoi(env);
@@ -204,10 +210,18 @@ AttnPlan plan_attn(const td_attn_args *a) {
   p.scale_log2 = scale * 1.4426950408889634f;
   p.decode = p.mfma && p.M <= 16 && a->B <= kDecodeMaxB;
   if (p.decode) {
-    // pieces of kDecodePieceKeys keys: sum over sequences of
-    // ceil((L_b + S) / piece) <= (total + B*S) / piece + B, per KV head
+    // blocks of kDecodeBlockKeys keys: sum over sequences of
+    // ceil((L_b + S) / 32) <= (total + B*S) / 32 + B, per KV head; one
+    // resident generation of waves, fewer when they would get under
+    // kDecodeMinBlocks blocks each.  Two partial slots per wave.  The choice
+    // only affects speed: any grid computes the same function.
     p.row_groups = 1;
-    p.units = int64_t(a->Hkv) * ((a->total_ctx + int64_t(a->B) * a->S) / kDecodePieceKeys + a->B + 1);
+    const int64_t blocks = int64_t(a->Hkv) * ((a->total_ctx + int64_t(a->B) * a->S) / kDecodeBlockKeys + a->B);
+    int64_t wgs = (blocks + int64_t(kDecodeWaves) * kDecodeMinBlocks - 1) / (int64_t(kDecodeWaves) * kDecodeMinBlocks);
+    wgs = std::max<int64_t>(1, std::min<int64_t>(wgs, kDecodeGridWGs));
+    const int forced = decode_grid_override();
+    p.launch = forced ? forced : int(wgs);
+    p.units = int64_t(2) * p.launch * kDecodeWaves;
     size_t o = 0;
     p.off_prefix = o; o += align256(size_t(a->B + 1) * 8);
     p.off_ml = o;     o += align256(size_t(p.units) * 16 * 8);

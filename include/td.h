@@ -327,9 +327,9 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
  * TD_NOALLOC_SCRATCH_BYTES returns TD_ERR_WORKSPACE.  With the default
  * launch plan, blocks of more than 16 query rows per KV head need 33 to 50
  * MiB whatever the batch; decode-shaped blocks (at most 16 query rows per KV
- * head) need about 4.2 KiB per 128 cached keys per KV head, so with 2 KV
- * heads caches beyond about 1M keys in total are rejected, as is a
- * TD_ATTN_GRID override well above the default.
+ * head) need at most about 17 MiB plus 8 bytes per sequence, whatever the
+ * context lengths.  A TD_ATTN_GRID or TD_DECODE_GRID override well above
+ * the default is rejected.
  * Every call on one GPU shares that GPU's array: calls that may overlap on
  * one GPU (different streams, or different threads without ordering) race
  * on it and must not be made.  Nothing in the array needs clearing between

@@ -91,11 +91,15 @@ def test_noalloc_limit_and_validation(L, monkeypatch):
     assert L.td_denoise_workspace_bytes(ctypes.byref(a), ctypes.byref(c)) > _td.TD_NOALLOC_SCRATCH_BYTES
     assert L.td_denoise_step_noalloc(ctypes.byref(a), ctypes.byref(c), None) == WORKSPACE
     monkeypatch.delenv("TD_ATTN_GRID")
-    # decode-shaped blocks over a very long packed cache: one partial per 128 keys
+    # decode-shaped blocks: two partial slots per wave, a size set by the
+    # grid alone; the default fits whatever the cache, 4096 workgroups do not
     d = attn(S=1, total_ctx=1 << 27, max_ctx=1 << 26)
     c1 = commit(S=1)
+    assert L.td_denoise_workspace_bytes(ctypes.byref(d), ctypes.byref(c1)) <= _td.TD_NOALLOC_SCRATCH_BYTES
+    monkeypatch.setenv("TD_DECODE_GRID", "4096")
     assert L.td_denoise_workspace_bytes(ctypes.byref(d), ctypes.byref(c1)) > _td.TD_NOALLOC_SCRATCH_BYTES
     assert L.td_denoise_step_noalloc(ctypes.byref(d), ctypes.byref(c1), None) == WORKSPACE
+    monkeypatch.delenv("TD_DECODE_GRID")
 
 
 def test_attn_empty_context_needs_no_context_pointers(L):
@@ -126,15 +130,19 @@ def test_attn_workspace_bytes(L):
 
 def test_attn_decode_workspace_bytes(L):
     """At most 16 query rows per KV head (here S = 1, 16 query heads per KV
-    head) take the decode path: one partial (16 x 128 bf16 O / l + 16 fp32
-    (m, l)) per piece of 128 keys, sized by the bound (total + B*S) / 128 +
-    B + 1 pieces per KV head, plus the per-sequence piece table."""
+    head) take the decode path: waves of 4 per workgroup, as many workgroups
+    as give each wave about 8 blocks of 32 keys (estimated as (total + B*S)
+    / 32 + B blocks per KV head), at most 512; two partial slots per wave
+    (16 x 128 bf16 O / l + 16 fp32 (m, l)), plus the per-sequence block
+    table."""
     def a256(x):
         return (x + 255) // 256 * 256
     for B, total, S, Hq, Hkv in [(64, 296372, 1, 32, 2), (3, 1000, 1, 32, 2), (1, 0, 1, 4, 1),
-                                 (7, 5000, 2, 16, 2)]:
+                                 (7, 5000, 2, 16, 2), (4, 1 << 20, 1, 32, 2)]:
         a = attn(B=B, S=S, Hq=Hq, Hkv=Hkv, total_ctx=total, max_ctx=total)
-        P = Hkv * ((total + B * S) // 128 + B + 1)
+        blocks = Hkv * ((total + B * S) // 32 + B)
+        wgs = max(1, min(512, -(-blocks // 32)))
+        P = 2 * 4 * wgs
         want = a256((B + 1) * 8) + a256(P * 16 * 8) + a256(P * 16 * 128 * 2)
         assert L.td_attn_workspace_bytes(ctypes.byref(a)) == want, (B, total, S)
 

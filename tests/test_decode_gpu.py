@@ -2,9 +2,10 @@
 KV head: G heads x S positions, G*S <= 16, bf16, D = 128), which
 td_block_attn takes by itself, against the fp64 oracle.  Gates as for the
 block path (tests/gpu_util.py): max abs <= 2e-2, mean abs <= 2e-3, relative
-L2 <= 1e-2 for bf16 inputs.  Cases span pieces of 256 keys with ragged
-tails, empty and one-key contexts, the batched cache at S = 1 (sampled),
-64K contexts, every G*S <= 16 split, and the gated step."""
+L2 <= 1e-2 for bf16 inputs.  Cases span splits of the 32-key blocks over
+1 to 4000 waves (units whole in one wave, or cut into pieces), empty and
+one-key contexts, the batched cache at S = 1 (sampled), 64K contexts, every
+G*S <= 16 split, and the gated step."""
 import numpy as np
 import pytest
 import torch
@@ -31,8 +32,8 @@ def test_decode_b64_ragged_sampled_and_deterministic():
 
 
 def test_decode_short_and_empty_contexts():
-    """Contexts of 0 .. 600 keys: single-piece units, empty caches (the one
-    block key only), pieces cut at 256 with ragged tails."""
+    """Contexts of 0 .. 600 keys: units of one to 19 blocks, empty caches (the
+    one block key only), ragged last blocks."""
     rng = np.random.default_rng(2002)
     lengths = rng.integers(0, 600, 50)
     lengths[:6] = [0, 1, 255, 256, 257, 511]
@@ -74,6 +75,23 @@ def test_decode_grid_override_has_no_effect(monkeypatch):
     second = run_attn(d, a)
     assert np.array_equal(first, second)
     check_attn(first, oracle_attn(a), "decode, grid override set")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 37, 512, 1000])
+def test_decode_grids(grid, monkeypatch):
+    """The decode split over waves: every wave streams an even run of 32-key
+    blocks, a unit cut between waves is merged from its pieces.  From one
+    workgroup (each unit whole or cut across few waves) to more waves than
+    blocks (capped: one block per wave, every unit cut into single-block
+    pieces), against the oracle."""
+    rng = np.random.default_rng(2010 + grid)
+    lengths = rng.integers(0, 3000, 5)
+    lengths[0] = 0
+    w = W["bf16_b8_ctx4k"].with_(B=5, S=1)
+    a = synth.make_attention_inputs(w, 2011 + grid, lengths=lengths)
+    monkeypatch.setenv("TD_DECODE_GRID", str(grid))
+    log(f"case decode grid={grid} lengths={lengths.tolist()}")
+    check_attn(run_attn(upload_attn(a), a), oracle_attn(a), f"decode grid {grid}")
 
 
 def test_decode_gated_step():

@@ -37,14 +37,17 @@
  *   Layouts    Row-major, innermost index last, no padding.
  *   Results    Deterministic: the same inputs give bitwise-identical outputs
  *              (no floating-point atomics; partials merged in a fixed order).
- *   Environment  Two variables override the launch plan, for testing the
- *              work split; results stay correct under either, only the
- *              speed changes:
+ *   Environment  Three variables override the launch plan, for testing the
+ *              work split; results stay correct under any, only the speed
+ *              changes:
  *                TD_ATTN_GRID=n     persistent attention workgroups (1..4096,
- *                                   default 256); it also sets the attention
- *                                   workspace size, so set it before the
- *                                   workspace query;
+ *                                   default 256);
+ *                TD_DECODE_GRID=n   workgroups of 4 waves of the decode-shaped
+ *                                   attention (at most 16 query rows per KV
+ *                                   head; 1..4096, default up to 512);
  *                TD_COMMIT_SPLIT=r  vocabulary slices per commit row.
+ *              The two grids also set the attention workspace size, so set
+ *              them before the workspace query.
  */
 #ifndef TD_H
 #define TD_H

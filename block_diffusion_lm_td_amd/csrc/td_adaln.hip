@@ -11,13 +11,14 @@
 //
 // adaln_rows: one 512-thread workgroup per sequence and run of R tokens.  Each
 // thread owns 8 consecutive hidden units per pass of 4096 (one 16-byte bf16
-// vector), and loads the modulation of its units (gate, w_norm * (1 + scale),
-// shift) to registers once for the R tokens.  Per token: the next token's x
-// and f are requested first (they stay in flight across the barrier, which
-// waits on LDS only), then the gated sum, its bf16 rounding and store, the
-// row's sum of squares reduced across the workgroup (one barrier,
-// double-buffered slot), then h.  Bound by HBM: x, f, r and h are 8 bytes per
-// element, the modulation rows are shared by a sequence's tokens.
+// vector).  At the start it requests, in the order they are needed, the
+// first token's x and f, the modulation of its units (gate, w_norm, scale,
+// shift: once for the R tokens), then the other tokens' x and f, so the whole
+// run is in flight at once and each token waits on its own rows only.  Per
+// token: the gated sum, its bf16 rounding and store, the row's sum of squares
+// reduced across the workgroup (one barrier, double-buffered slot), then h.
+// Bound by HBM: x, f, r and h are 8 bytes per element, streamed with the
+// non-temporal hint; the modulation rows are shared by a sequence's tokens.
 #include <hip/hip_runtime.h>
 
 #include "td_internal.h"
@@ -26,6 +27,19 @@ namespace td {
 namespace {
 
 typedef __bf16 bf16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// x, f, r and h are each touched once per call: their rows are streamed with
+// the non-temporal hint, so they do not displace the modulation rows that a
+// sequence's workgroups share in L2
+__device__ inline uint4 ld_stream(const void *p) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ inline void st_stream(void *p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
 
 constexpr int kThreadsA = 512;                  // 8 waves
 constexpr int kColsPerPass = kThreadsA * 8;
@@ -45,27 +59,26 @@ __device__ inline uint32_t pack2(float a, float b) {
 __device__ inline uint4 pack8(const float v[8]) {
   return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
-// 8 floats at p (32-byte aligned), or `fill` when p is null
-__device__ inline void ld8f(const float *p, float o[8], float fill) {
-  if (!p) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = fill;
-    return;
-  }
+// stands in for an absent [H] table row (zero-initialised device memory), so
+// that every load is unconditional and the waits on them can be counted
+__device__ float kZeroRow[8192];
+
+// 8 floats at p (32-byte aligned)
+__device__ inline void ld8f(const float *p, float o[8]) {
   const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
   o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
-template <int PASSES>
+template <int PASSES, int RT, bool GATED>
 __global__ __launch_bounds__(kThreadsA) void adaln_rows(
-    const bf16 *x, const bf16 *f, const float *__restrict__ t_mod,   // x, f may be r_out or h
-    const float *__restrict__ tab_gate, const float *__restrict__ tab_shift,
-    const float *__restrict__ tab_scale, const float *__restrict__ w_norm, bf16 *r_out, bf16 *h,
-    int S, int H, int R, float eps) {
+    const bf16 *x, const bf16 *f, const float *t_mod,   // x, f may be r_out or h
+    const float *tab_gate, const float *tab_shift, const float *tab_scale, const float *w_norm,
+    bf16 *r_out, bf16 *h,
+    int S, int H, float eps) {
   __shared__ float s_red[2][kThreadsA / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int runs = (S + R - 1) / R;
+  const int runs = (S + RT - 1) / RT;
   // workgroups are dealt to the 8 XCDs in turn: within each window of 8
   // sequences, XCD x takes all runs of the window's sequence x, so that the
   // sequence's timestep rows are fetched into one L2 only
@@ -74,98 +87,106 @@ __global__ __launch_bounds__(kThreadsA) void adaln_rows(
                            ? bid
                            : bid / win * win + unsigned(runs) * (bid & 7u) + (bid >> 3) % unsigned(runs);
   const int b = int(lwg / unsigned(runs));
-  const int s0 = (int(lwg) - b * runs) * R, s1 = min(S, s0 + R);
+  const int s0 = (int(lwg) - b * runs) * RT, s1 = min(S, s0 + RT);
   const float *tm = t_mod + int64_t(b) * 3 * H;
+  const float *tg = tab_gate ? tab_gate : kZeroRow, *ts = tab_shift ? tab_shift : kZeroRow;
+  const float *tc = tab_scale ? tab_scale : kZeroRow, *wn = w_norm ? w_norm : kZeroRow;
+  const float w_add = w_norm ? 0.f : 1.f;          // an absent weight is all ones
 
-  // this thread's units: 8 * (tid + 256 k), k < PASSES (past H: unused)
-  float gt[PASSES][8], sc[PASSES][8], sh[PASSES][8];
+  // this thread's units: 8 * (tid + 512 k), k < PASSES.  Past H a lane loads
+  // the last 8 units (in bounds) and stores nothing.
+  int col[PASSES];
+  bool live[PASSES];
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
-    const int col = 8 * (tid + kThreadsA * k);
-    if (col >= H) continue;
-    float t[8], u[8];
-    ld8f(tm + col, sh[k], 0.f);                    // t_mod row 0: shift
-    ld8f(tab_shift ? tab_shift + col : nullptr, t, 0.f);
-    ld8f(tm + H + col, sc[k], 0.f);                // row 1: scale
-    ld8f(tab_scale ? tab_scale + col : nullptr, u, 0.f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sh[k][i] += t[i];
-      sc[k][i] = 1.f + (sc[k][i] + u[i]);
-    }
-    ld8f(w_norm ? w_norm + col : nullptr, t, 1.f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sc[k][i] *= t[i];   // w_norm * (1 + scale)
-    if (f) {
-      ld8f(tm + 2 * H + col, gt[k], 0.f);          // row 2: gate
-      ld8f(tab_gate ? tab_gate + col : nullptr, t, 0.f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gt[k][i] += t[i];
-    }
+    const int c = 8 * (tid + kThreadsA * k);
+    live[k] = c < H;
+    col[k] = min(c, H - 8);
   }
-
-  const float inv_h = 1.f / float(H);
-  uint4 xq[PASSES], fq[PASSES];
-  {
-    const int64_t row = (int64_t(b) * S + s0) * H;
+  // requested in the order they are needed: the first token's x and f, the
+  // modulation rows, then the other tokens of the run (a run shorter than RT
+  // re-reads its last row), so the whole run is in flight at the start and
+  // each token waits only on its own rows
+  uint4 xq[RT][PASSES], fq[RT][PASSES];
+  auto load_token = [&](int t) {
+    const int64_t row = (int64_t(b) * S + min(s0 + t, s1 - 1)) * H;
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int col = 8 * (tid + kThreadsA * k);
-      if (col >= H) continue;
-      xq[k] = *reinterpret_cast<const uint4 *>(x + row + col);
-      if (f) fq[k] = *reinterpret_cast<const uint4 *>(f + row + col);
+      xq[t][k] = ld_stream(x + row + col[k]);
+      if (GATED) fq[t][k] = ld_stream(f + row + col[k]);
+    }
+  };
+  load_token(0);
+  float gt[PASSES][8], sc[PASSES][8], sh[PASSES][8], t0[PASSES][8], t1[PASSES][8], t2[PASSES][8],
+      t3[PASSES][8];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    ld8f(tm + col[k], sh[k]);                      // t_mod row 0: shift
+    ld8f(ts + col[k], t0[k]);
+    ld8f(tm + H + col[k], sc[k]);                  // row 1: scale
+    ld8f(tc + col[k], t1[k]);
+    ld8f(wn + col[k], t2[k]);
+    if (GATED) {
+      ld8f(tm + 2 * H + col[k], gt[k]);            // row 2: gate
+      ld8f(tg + col[k], t3[k]);
     }
   }
-  for (int s = s0; s < s1; ++s) {
-    const int64_t row = (int64_t(b) * S + s) * H;
-    uint4 rv[PASSES], fc[PASSES];
 #pragma unroll
-    for (int k = 0; k < PASSES; ++k) { rv[k] = xq[k]; fc[k] = fq[k]; }
-    if (s + 1 < s1) {
+  for (int t = 1; t < RT; ++t) load_token(t);
+  // keep every load ahead of the first use: the empty asm stops the loads
+  // from being sunk to their uses, the barrier stops the scheduler
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < PASSES; ++k) {
-        const int col = 8 * (tid + kThreadsA * k);
-        if (col >= H) continue;
-        xq[k] = *reinterpret_cast<const uint4 *>(x + row + H + col);
-        if (f) fq[k] = *reinterpret_cast<const uint4 *>(f + row + H + col);
-      }
+  for (int k = 0; k < PASSES; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sh[k][i] += t0[k][i];
+      sc[k][i] = (1.f + (sc[k][i] + t1[k][i])) * (t2[k][i] + w_add);   // w_norm * (1 + scale)
+      if (GATED) gt[k][i] += t3[k][i];
     }
+
+  const float inv_h = 1.f / float(H);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int s = s0 + t;
+    if (s >= s1) break;
+    const int64_t row = (int64_t(b) * S + s) * H;
+    uint4 rv[PASSES];
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int col = 8 * (tid + kThreadsA * k);
-      if (col >= H) continue;
-      if (f) {
+      rv[k] = xq[t][k];
+      if (GATED) {
         float xv[8], fv[8];
         unpack8(rv[k], xv);
-        unpack8(fc[k], fv);
+        unpack8(fq[t][k], fv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) xv[i] = __builtin_fmaf(gt[k][i], fv[i], xv[i]);
         rv[k] = pack8(xv);
-        *reinterpret_cast<uint4 *>(r_out + row + col) = rv[k];
+        if (live[k]) st_stream(r_out + row + col[k], rv[k]);
       }
-      float rr[8];
+      float rr[8], q = 0.f;
       unpack8(rv[k], rr);                          // the stored (rounded) r
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(rr[i], rr[i], ss);
+      for (int i = 0; i < 8; ++i) q = __builtin_fmaf(rr[i], rr[i], q);
+      ss += live[k] ? q : 0.f;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    if (lane == 0) s_red[s & 1][wv] = ss;
-    __syncthreads();                               // slot s&1 is next written two tokens on
+    if (lane == 0) s_red[t & 1][wv] = ss;
+    __syncthreads();                               // slot t&1 is next written two tokens on
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreadsA / 64; ++w) tot += s_red[s & 1][w];
+    for (int w = 0; w < kThreadsA / 64; ++w) tot += s_red[t & 1][w];
     const float rinv = rsqrtf(tot * inv_h + eps);
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int col = 8 * (tid + kThreadsA * k);
-      if (col >= H) continue;
       float rr[8];
       unpack8(rv[k], rr);
 #pragma unroll
       for (int i = 0; i < 8; ++i) rr[i] = __builtin_fmaf(rr[i] * rinv, sc[k][i], sh[k][i]);
-      *reinterpret_cast<uint4 *>(h + row + col) = pack8(rr);
+      if (live[k]) st_stream(h + row + col[k], pack8(rr));
     }
   }
 }
@@ -175,8 +196,8 @@ __global__ __launch_bounds__(kThreadsA) void adaln_rows(
 int launch_adaln(const td_adaln_args *a, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // tokens per workgroup: the most that still leaves a workgroup per CU (more
-  // tokens amortise the modulation loads and pipeline the rows; at 64 x 16 x
-  // 4096, 4 tokens take 11.4 us against 12.4 us for 2 and 14.0 us for 8)
+  // tokens amortise the modulation loads and put more rows in flight; at
+  // 64 x 16 x 4096, 4 tokens take 10.0 us against 12.0 us for 2)
   int R = 1;
   for (int r : {8, 4, 2})
     if (int64_t(a->B) * ((a->S + r - 1) / r) >= 256) {
@@ -185,14 +206,22 @@ int launch_adaln(const td_adaln_args *a, void *stream) {
     }
   const dim3 grid(unsigned(int64_t(a->B) * ((a->S + R - 1) / R))), block(kThreadsA);
   const int passes = (a->H + kColsPerPass - 1) / kColsPerPass;
-#define TD_ADALN(PS)                                                                                \
-  hipLaunchKernelGGL((adaln_rows<PS>), grid, block, 0, st, static_cast<const bf16 *>(a->x),        \
+#define TD_ADALN(PS, RR)                                                                            \
+  hipLaunchKernelGGL((a->f ? adaln_rows<PS, RR, true> : adaln_rows<PS, RR, false>), grid, block, 0, st, static_cast<const bf16 *>(a->x),    \
                      static_cast<const bf16 *>(a->f), a->t_mod, a->tab_gate, a->tab_shift,          \
                      a->tab_scale, a->w_norm, static_cast<bf16 *>(a->r_out), static_cast<bf16 *>(a->h), \
-                     a->S, a->H, R, a->eps)
-  if (passes <= 1) TD_ADALN(1);
-  else if (passes <= 2) TD_ADALN(2);                // H <= 8192
+                     a->S, a->H, a->eps)
+#define TD_ADALN_R(PS)                                                                              \
+  switch (R) {                                                                                      \
+    case 8: TD_ADALN(PS, 8); break;                                                                 \
+    case 4: TD_ADALN(PS, 4); break;                                                                 \
+    case 2: TD_ADALN(PS, 2); break;                                                                 \
+    default: TD_ADALN(PS, 1); break;                                                                \
+  }
+  if (passes <= 1) TD_ADALN_R(1)
+  else if (passes <= 2) TD_ADALN_R(2)               // H <= 8192
   else return TD_ERR_UNSUPPORTED;
+#undef TD_ADALN_R
 #undef TD_ADALN
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }

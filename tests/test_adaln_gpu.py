@@ -132,13 +132,17 @@ def test_adaln_optional_inputs(use_f, tables):
     _check(r, h, d, f"f={use_f} tables={tables}", use_f=use_f, tables=tables, eps=1e-3)
 
 
+@pytest.mark.parametrize("B,S,H", [
+    (64, 16, 1024),     # 4 tokens per workgroup, whole runs
+    (150, 5, 256),      # 4 per workgroup, a ragged last run of 1 (its spare loads re-read the row it writes)
+])
 @pytest.mark.parametrize("mode", ["r_is_x", "h_is_f", "h_is_x"])
-def test_adaln_in_place(mode):
-    w = AW["adaln_exact_b4_s16_h256"].with_(B=64, S=16, H=1024)
+def test_adaln_in_place(mode, B, S, H):
+    w = AW["adaln_exact_b4_s16_h256"].with_(B=B, S=S, H=H)
     d = synth.make_adaln_inputs(w, 85)
-    log(f"case adaln in place {mode}")
+    log(f"case adaln in place {mode} B{B} S{S} H{H}")
     r, h = _run(d, inplace=mode)
-    _check(r, h, d, f"in place {mode}", exact=True)
+    _check(r, h, d, f"in place {mode} B{B} S{S} H{H}", exact=True)
 
 
 def test_adaln_batched_and_deterministic():

@@ -674,21 +674,29 @@ __global__ __launch_bounds__(kWGThreads, 1) void attn_bf16_mfma(
   }
 }
 
-// Merge of the partials of every unit cut between workgroups: one workgroup
-// per (unit, 32-row block of one wave); thread (db, lane) combines the 16
-// values that lane held in fragment db, over the unit's pieces in workgroup
-// order with a running max (one pass, deterministic).  PRE pieces are
-// fetched per memory round trip: 4 keeps the registers (and the occupancy)
-// of the common case of a few pieces per unit; 16 serves long contexts,
-// whose units are cut into dozens of pieces.
-template <int PRE>
+// Merge of the partials of every unit cut between workgroups.  A 32-row block
+// of one wave's rows is merged by PG workgroups of 256 threads, each taking
+// 32/PG of its rows; inside a workgroup PG thread groups split the unit's
+// pieces round-robin (group q takes pieces q, q + PG, ...).  A thread (db, lh,
+// row) combines the 16 values of fragment db that lane (lh, row) held, over
+// its group's pieces in workgroup order with a running max; the groups'
+// states are then combined in group order through LDS (deterministic).  PRE
+// pieces are fetched per memory round trip.  PG = 1, PRE = 4 serves the
+// common case of a few pieces per unit; long contexts over few sequences cut
+// each unit into dozens of pieces, and PG = 4, PRE = 8 spreads them over four
+// times the workgroups and threads.
+template <int PRE, int PG>
 __device__ __forceinline__ void merge_block(
     int64_t blk, const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M,
     int RG, int P, const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o,
     bf16 *__restrict__ out) {
+  constexpr int RW = 32 / PG;                      // rows of this workgroup
+  constexpr int TG = 256 / PG;                     // threads per piece group
+  static_assert(PG == 1 || PG == 2 || PG == 4 || PG == 8, "piece groups");
   const int UPS = Hkv * RG;
-  const int64_t u = blk >> 3;
-  const int w = int(blk & 7);
+  const int64_t u = blk / (8 * PG);
+  const int w = int((blk / PG) & 7);
+  const int sb = int(blk % PG);
   const int b = int(u / UPS), uis = int(u - (u / UPS) * UPS);
   const int g = uis / RG, rg = uis - (uis / RG) * RG;
   const int64_t W = prefix[B] * UPS;
@@ -698,11 +706,14 @@ __device__ __forceinline__ void merge_block(
   const int64_t Cu = UPS * (prefix[b] + int64_t(kSegCost) * b) + int64_t(uis) * (n + kSegCost);
   const int64_t y0 = Cu + kSegCost;               // cost slots of the unit's first and last tiles
   const int64_t p_first = slot_owner(y0, C, Pe), p_last = slot_owner(y0 + n - 1, C, Pe);
-  if (p_first == p_last) return;                 // written whole by its workgroup
-  const int lane = threadIdx.x & 63, db = threadIdx.x >> 6;
-  const int lq = lane & 31, lh = lane >> 5;
+  if (p_first == p_last) return;                 // written whole by its workgroup (uniform)
+  const int pg = threadIdx.x / TG, t = threadIdx.x - pg * TG;
+  const int db = t / (2 * RW), r2 = t - db * (2 * RW);
+  const int lh = r2 / RW, lq = sb * RW + (r2 - lh * RW);
+  const int lane = lh * 32 + lq;
   const int row = rg * kRowsPerWG + w * 32 + lq;
-  if (row >= M) return;
+  const bool live = row < M;
+  if (PG == 1 && !live) return;                  // no barrier below with one group
   const uint4 *wo = reinterpret_cast<const uint4 *>(ws_o);
   float mx = kNegInf, lsum = 0.f;
   float acc[16];
@@ -734,19 +745,49 @@ __device__ __forceinline__ void merge_block(
       acc[2 * i + 1] += wgt * __uint_as_float(h[i] & 0xffff0000u);
     }
   };
-  // pieces are fetched kPre at a time (one memory round trip per batch) and
+  // this group's pieces, PRE at a time (one memory round trip per batch),
   // combined in workgroup order
-  constexpr int kPre = PRE;
-  for (int64_t base = p_first; base <= p_last; base += kPre) {
-    float2 mlv[kPre];
-    uint4 xa[kPre], xb[kPre];
+  if (live) {
+    for (int64_t base = p_first + pg; base <= p_last; base += int64_t(PRE) * PG) {
+      float2 mlv[PRE];
+      uint4 xa[PRE], xb[PRE];
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
-      if (base + k <= p_last) fetch(base + k, mlv[k], xa[k], xb[k]);
+      for (int k = 0; k < PRE; ++k)
+        if (base + int64_t(k) * PG <= p_last) fetch(base + int64_t(k) * PG, mlv[k], xa[k], xb[k]);
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
-      if (base + k <= p_last) absorb(mlv[k], xa[k], xb[k]);
+      for (int k = 0; k < PRE; ++k)
+        if (base + int64_t(k) * PG <= p_last) absorb(mlv[k], xa[k], xb[k]);
+    }
   }
+  if constexpr (PG > 1) {
+    // the groups' states meet in LDS; group 0 folds groups 1.. in order
+    __shared__ float s_st[PG - 1][18][TG];
+    if (pg > 0) {
+      s_st[pg - 1][0][t] = mx;
+      s_st[pg - 1][1][t] = lsum;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_st[pg - 1][2 + i][t] = acc[i];
+    }
+    __syncthreads();
+    if (pg > 0 || !live) return;
+#pragma unroll
+    for (int q = 0; q < PG - 1; ++q) {
+      const float qm = s_st[q][0][t], ql = s_st[q][1][t];
+      if (ql == 0.f) continue;                     // a group with no pieces
+      if (qm > mx) {
+        const float c = fast_exp2(mx - qm);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] *= c;
+        lsum *= c;
+        mx = qm;
+      }
+      const float c = fast_exp2(qm - mx);
+      lsum += ql * c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += s_st[q][2 + i][t] * c;
+    }
+  }
+  if (!live) return;
   const float inv = 1.0f / lsum;
   const int s = row / G, jh = row - (row / G) * G;
   bf16 *dst = out + ((int64_t(b) * S + s) * Hq + int64_t(g) * G + jh) * HD + db * 32 + lh * 4;
@@ -757,13 +798,13 @@ __device__ __forceinline__ void merge_block(
                    pack_bf16(acc[gi * 4 + 2] * inv, acc[gi * 4 + 3] * inv));
 }
 
-template <int PRE>
+template <int PRE, int PG>
 __global__ __launch_bounds__(256) void attn_merge(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
     const int32_t *__restrict__ gate) {
   if (gate && *gate == 0) return;
-  merge_block<PRE>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+  merge_block<PRE, PG>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
 }
 
 // The tail of a denoise step in one launch: the attention merge (blocks
@@ -771,7 +812,7 @@ __global__ __launch_bounds__(256) void attn_merge(
 // decision (the remaining blocks, one wave per sequence, as
 // commit_finalize).  The two share no data; running them in one grid saves
 // a launch and its drain on the step's critical path.
-template <int PRE>
+template <int PRE, int PG>
 __global__ __launch_bounds__(256) void step_tail(
     const int64_t *__restrict__ prefix, int B, int S, int Hq, int Hkv, int G, int M, int RG, int P,
     const float2 *__restrict__ ws_ml, const bf16 *__restrict__ ws_o, bf16 *__restrict__ out,
@@ -782,7 +823,7 @@ __global__ __launch_bounds__(256) void step_tail(
     const int32_t *__restrict__ gate) {
   if (gate && *gate == 0) return;
   if (int64_t(blockIdx.x) < merge_blocks) {
-    merge_block<PRE>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
+    merge_block<PRE, PG>(blockIdx.x, prefix, B, S, Hq, Hkv, G, M, RG, P, ws_ml, ws_o, out);
     return;
   }
   const int b = int(int64_t(blockIdx.x) - merge_blocks) * 4 + int(threadIdx.x >> 6);
@@ -893,8 +934,9 @@ int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream
                        a->B, a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, p.scale_log2,
                        prefix, ws_ml, ws_o, static_cast<bf16 *>(a->out), gate);
     if (merge) {
-      auto k = many_pieces(p) ? attn_merge<16> : attn_merge<4>;
-      hipLaunchKernelGGL(k, dim3(unsigned(p.units * 8)), dim3(256), 0, st, prefix, a->B,
+      const bool many = many_pieces(p);
+      auto k = many ? attn_merge<8, 4> : attn_merge<4, 1>;
+      hipLaunchKernelGGL(k, dim3(unsigned(p.units * 8 * (many ? 4 : 1))), dim3(256), 0, st, prefix, a->B,
                          a->S, a->Hq, a->Hkv, p.G, p.M, p.row_groups, p.launch, ws_ml, ws_o,
                          static_cast<bf16 *>(a->out), gate);
     }
@@ -916,9 +958,10 @@ int launch_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws, const t
                      const CommitPlan &pc, void *ws_commit, void *stream, const int32_t *gate) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char *wsb = static_cast<char *>(ws);
-  const int64_t merge_blocks = p.units * 8;
+  const bool many = many_pieces(p);
+  const int64_t merge_blocks = p.units * 8 * (many ? 4 : 1);
   const int64_t fin_blocks = (int64_t(c->B) + 3) / 4;
-  auto k = many_pieces(p) ? step_tail<16> : step_tail<4>;
+  auto k = many ? step_tail<8, 4> : step_tail<4, 1>;
   hipLaunchKernelGGL(k, dim3(unsigned(merge_blocks + fin_blocks)), dim3(256), 0, st,
                      reinterpret_cast<int64_t *>(wsb + p.off_prefix), a->B, a->S, a->Hq, a->Hkv, p.G,
                      p.M, p.row_groups, p.launch, reinterpret_cast<float2 *>(wsb + p.off_ml),

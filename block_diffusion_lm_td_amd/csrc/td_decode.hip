@@ -12,10 +12,11 @@
 // started); every wave streams its run of blocks once, after one prologue:
 //   - Each 32-key block comes from HBM into registers with ordinary 16-byte
 //     loads: K already in the MFMA operand layout (each lane 16 bytes of one
-//     key row per MFMA), V in 16-byte chunks.  Two register sets alternate,
-//     so every wave keeps the next block in flight while it works on the
-//     current one (a stream needs many bytes in flight; the register file
-//     holds them, the LDS only the one block being transposed).
+//     key row per MFMA), V in 16-byte chunks.  Three register sets rotate,
+//     so every wave keeps the next two blocks in flight while it works on
+//     the current one (a stream needs many bytes in flight; the register
+//     file holds them, the LDS only the one block being transposed).  That
+//     takes one wave per SIMD: one workgroup of 4 waves per CU.
 //   - S^T = K Q^T in 16-key tiles.
 //   - O^T += V^T P^T: the V block goes into the wave's own LDS slot (no
 //     barriers), row-major with 16-byte chunks XOR-swizzled by 2*(row % 8),
@@ -46,6 +47,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 constexpr int HD = 128;
 constexpr int kBlk = kDecodeBlockKeys;     // keys per step
 constexpr int kDecWaves = kDecodeWaves;
+constexpr int kSets = 3;                   // register sets of K and V blocks: two in flight while one is worked on
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -87,7 +89,7 @@ __device__ inline int64_t dec_owner(int64_t y, int64_t C, int64_t NW) { return (
 // One wave per range of blocks.  Every workgroup scans the blocks per
 // sequence into LDS (B <= kDecodeMaxB); workgroup 0 also leaves the prefix
 // in the workspace for the merge.
-__global__ __launch_bounds__(kDecWaves * 64, 2) void attn_decode(
+__global__ __launch_bounds__(kDecWaves * 64, 1) void attn_decode(
     const bf16 *__restrict__ q, const bf16 *__restrict__ kb, const bf16 *__restrict__ vb,
     const bf16 *__restrict__ kc, const bf16 *__restrict__ vc, const int64_t *__restrict__ off,
     int64_t total, int max_ctx, int B, int S, int Hq, int Hkv, int G, float sl2,
@@ -293,18 +295,23 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void attn_decode(
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a01), pt, o[dt], 0, 0, 0);
       }
     };
-    // two register sets: block jb + 1 loads while block jb is processed.  The
-    // loads are unconditional (past the segment they re-read a valid block,
-    // cached): behind a branch, the compiler would wait for every load in
-    // flight, the next block's included, before using the current one.
-    Blk b0, b1;
-    load_blk(j0, b0);
-    for (int jb = j0; jb < j1; jb += 2) {
-      load_blk(jb + 1 < j1 ? jb + 1 : jb, b1);
-      step(jb, b0);
-      if (jb + 1 >= j1) break;
-      load_blk(jb + 2 < j1 ? jb + 2 : jb + 1, b0);
-      step(jb + 1, b1);
+    // kSets register sets in rotation: blocks jb + 1 .. jb + kSets - 1 load
+    // while block jb is processed (the set of block jb is reloaded only after
+    // its step).  The loop is unrolled over the sets so that each keeps its
+    // registers.  The loads are unconditional (past the segment they re-read
+    // a valid block, cached): behind a branch, the compiler would wait for
+    // every load in flight, the next blocks' included, before using the
+    // current one.
+    Blk bs[kSets];
+#pragma unroll
+    for (int q = 0; q < kSets - 1; ++q) load_blk(min(j0 + q, j1 - 1), bs[q]);
+    for (int jb = j0; jb < j1; jb += kSets) {
+#pragma unroll
+      for (int q = 0; q < kSets; ++q) {
+        if (jb + q >= j1) break;
+        load_blk(min(jb + q + kSets - 1, j1 - 1), bs[(q + kSets - 1) % kSets]);
+        step(jb + q, bs[q]);
+      }
     }
     // l: the four lanes of a query hold disjoint keys
     l += __shfl_xor(l, 16);

@@ -17,7 +17,7 @@ constexpr int kWGThreads = 64 * kWaves;
 constexpr int kGridWGs = 256;     // persistent grid: one workgroup per CU of MI355X
 constexpr int kDecodeBlockKeys = 32;    // keys per block of the decode path
 constexpr int kDecodeWaves = 4;         // waves per decode workgroup
-constexpr int kDecodeGridWGs = 512;     // one resident generation: two workgroups per CU
+constexpr int kDecodeGridWGs = 256;     // one resident generation: one workgroup per CU
 constexpr int kDecodeMinBlocks = 8;     // fewer waves below about 8 blocks each
 constexpr int kDecodeMaxB = 4096;       // sequences whose piece table fits the decode kernel's LDS
 

@@ -44,7 +44,7 @@
  *                                   default 256);
  *                TD_DECODE_GRID=n   workgroups of 4 waves of the decode-shaped
  *                                   attention (at most 16 query rows per KV
- *                                   head; 1..4096, default up to 512);
+ *                                   head; 1..4096, default up to 256);
  *                TD_COMMIT_SPLIT=r  vocabulary slices per commit row.
  *              The two grids also set the attention workspace size, so set
  *              them before the workspace query.
@@ -330,7 +330,7 @@ int td_denoise_step_if(const td_attn_args *a, const td_commit_args *c, const int
  * TD_NOALLOC_SCRATCH_BYTES returns TD_ERR_WORKSPACE.  With the default
  * launch plan, blocks of more than 16 query rows per KV head need 33 to 50
  * MiB whatever the batch; decode-shaped blocks (at most 16 query rows per KV
- * head) need at most about 17 MiB plus 8 bytes per sequence, whatever the
+ * head) need at most about 9 MiB plus 8 bytes per sequence, whatever the
  * context lengths.  A TD_ATTN_GRID or TD_DECODE_GRID override well above
  * the default is rejected.
  * Every call on one GPU shares that GPU's array: calls that may overlap on

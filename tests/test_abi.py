@@ -132,7 +132,7 @@ def test_attn_decode_workspace_bytes(L):
     """At most 16 query rows per KV head (here S = 1, 16 query heads per KV
     head) take the decode path: waves of 4 per workgroup, as many workgroups
     as give each wave about 8 blocks of 32 keys (estimated as (total + B*S)
-    / 32 + B blocks per KV head), at most 512; two partial slots per wave
+    / 32 + B blocks per KV head), at most 256; two partial slots per wave
     (16 x 128 bf16 O / l + 16 fp32 (m, l)), plus the per-sequence block
     table."""
     def a256(x):
@@ -141,7 +141,7 @@ def test_attn_decode_workspace_bytes(L):
                                  (7, 5000, 2, 16, 2), (4, 1 << 20, 1, 32, 2)]:
         a = attn(B=B, S=S, Hq=Hq, Hkv=Hkv, total_ctx=total, max_ctx=total)
         blocks = Hkv * ((total + B * S) // 32 + B)
-        wgs = max(1, min(512, -(-blocks // 32)))
+        wgs = max(1, min(256, -(-blocks // 32)))
         P = 2 * 4 * wgs
         want = a256((B + 1) * 8) + a256(P * 16 * 8) + a256(P * 16 * 128 * 2)
         assert L.td_attn_workspace_bytes(ctypes.byref(a)) == want, (B, total, S)

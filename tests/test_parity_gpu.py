@@ -77,6 +77,22 @@ def test_attn_bf16_shapes(S, Hq, Hkv):
     check_attn(got, oracle_attn(a), f"S={S} Hq={Hq} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv", [(16, 64, 8), (4, 32, 8), (1, 8, 1)])
+def test_attn_gqa_long_ragged(S, Hq, Hkv):
+    """Other GQA groupings over long ragged contexts, every sequence: G = 8
+    with 128 live rows of each 256-row group (block path), and G*S = 16 and 8
+    (decode path) with contexts from 3 to 20K keys."""
+    w = W["bf16_b8_ctx4k"].with_(B=6, S=S, Hq=Hq, Hkv=Hkv)
+    a = synth.make_attention_inputs(w, 300 + S + Hq, lengths=[16000, 3, 9000, 20000, 64, 4097])
+    log("case attn gqa long ragged", S, Hq, Hkv)
+    d = upload_attn(a)
+    got = run_attn(d, a)
+    check_attn(got, oracle_attn(a), f"gqa long S={S} Hq={Hq} Hkv={Hkv}")
+    first = d["out"].clone()
+    run_attn(d, a)
+    assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
+
+
 def _random_attn_cases(n=24, seed=4242):
     """Seeded random valid shapes: ragged lengths with empty and sub-tile
     contexts and tile-edge lengths, S from 1 to 64, several GQA groupings,

@@ -26,6 +26,10 @@
 //   - Tiles are numbered with the position tile fastest and dealt to the
 //     XCDs in contiguous ranges, so the position tiles that share a slice of
 //     the head run together on one XCD and read it from its L2.
+//   - When at most 128 positions are left (a block's late steps) the tiles
+//     are 256 x 128 with a 3-stage ring of 48 KiB stages: one position tile
+//     then streams the head, and two head stages in flight instead of one
+//     take such a call from about 258 to 192 us.
 //   Measured at 64 x 16 positions, H = 4096, V = 131072, every position
 //   scored (median of 7 x 20 launches of td_lmhead_commit): 879 us, against
 //   927 us for the same tiles on 32x32x16 blocks.  Earlier 32x32x16 layouts:
@@ -54,6 +58,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGrid = 256;        // persistent: one workgroup per CU of MI355X
 constexpr int kRowBytes = kTK * 2;
 constexpr int kStageBytes = (kTN + kTM) * kRowBytes;
+constexpr int kTMSmall = 128;     // positions per tile when at most this many are left
+constexpr int kRingBytes = kStages * kStageBytes > 3 * (kTN + kTMSmall) * kRowBytes
+                               ? kStages * kStageBytes
+                               : 3 * (kTN + kTMSmall) * kRowBytes;
 constexpr int kRPB = 256 / kRowBytes;          // rows per 256 bytes
 constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
 constexpr int kRPI = 1024 / kRowBytes;         // rows per 1 KiB DMA instruction
@@ -149,22 +157,31 @@ __global__ __launch_bounds__(1024) void lmhead_compact(const uint8_t *__restrict
 
 // Persistent: one workgroup per CU (kGrid, a multiple of 8) loops over the
 // tiles.  rows / count: the compacted positions (NULL: all M positions in
-// order); only the ceil(count / 256) position tiles that hold positions are
+// order); only the ceil(count / TM) position tiles that hold positions are
 // visited.  Tiles are numbered with the position tile fastest; XCD x (the
 // workgroups b with b % 8 == x) takes a contiguous range of them, its
 // workgroups in turn, so the position tiles of one head slice run at the
 // same time on one XCD and share the slice through its L2.
-template <bool kPacked>
-__global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
-    const bf16 *__restrict__ hidden, const bf16 *__restrict__ whead, int M, int V, int H,
-    int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
-    Part *__restrict__ parts) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
+//
+// TM positions per tile: 256 with a 2-stage ring of 64 KiB stages, or, when
+// at most 128 positions are left (a block's late steps), 128 with a 3-stage
+// ring of 48 KiB stages.  Then only one position tile exists and a pass over
+// the head is bound by its stream, so two stages of the head are kept in
+// flight instead of one; each wave takes 64 head rows x 32 positions.
+template <bool kPacked, int TM>
+__device__ __forceinline__ void tiles_body(unsigned char *ring, const bf16 *__restrict__ hidden,
+                                           const bf16 *__restrict__ whead, int Mc, int V, int H,
+                                           int n_tiles, const int32_t *__restrict__ rows,
+                                           Part *__restrict__ parts) {
+  constexpr int NST = TM == kTM ? kStages : 3;           // ring stages
+  constexpr int SB = (kTN + TM) * kRowBytes;             // bytes per stage
+  constexpr int IPWH = TM * kRowBytes / 1024 / kWaves;   // hidden DMA instructions per wave
+  constexpr int TMWv = TM / WM, NJv = TMWv / kMB;
+  static_assert(NST * SB <= kRingBytes && IPWH >= 1 && NJv >= 1, "tile shape");
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
   const int wn = w % WN, wm = w / WN;
-  const int Mc = count ? *count : M;
-  const int m_act = (Mc + kTM - 1) / kTM;
+  const int m_act = (Mc + TM - 1) / TM;
   const int n_act = m_act * n_tiles;
   const int x = blockIdx.x & 7, px = blockIdx.x >> 3, PX = gridDim.x >> 3;
   const int q = n_act >> 3, r8 = n_act & 7;
@@ -172,19 +189,25 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
   for (int j = px; j < x_n; j += PX) {
     const int t = x_lo + j;
     const int tn = t / m_act, tm = t - tn * m_act;
-    const int n0 = tn * kTN, m0 = tm * kTM;
-    uint32_t voff_w[kIPW], voff_h[kIPW];
+    const int n0 = tn * kTN, m0 = tm * TM;
+    uint32_t voff_w[kIPW], voff_h[IPWH];
 #pragma unroll
     for (int u = 0; u < kIPW; ++u) {
       const int i = w + kWaves * u;
       const int row = kRPI * i + lane / kCPR;
       const int c = (lane % kCPR) ^ swz(row);
       const int rw = min(n0 + row, V - 1) - n0;     // row-major: rows past V re-read row V-1
-      const int cm = min(m0 + row, Mc - 1);
-      const int rh = rows ? rows[cm] : cm;        // hidden row of this position
       // packed: the stage's 256 x 64 block is contiguous, rows past V are zeros
       voff_w[u] = kPacked ? uint32_t(row) * uint32_t(kRowBytes) + uint32_t(c) * 16u
                           : uint32_t(rw) * uint32_t(H) * 2u + uint32_t(c) * 16u;
+    }
+#pragma unroll
+    for (int u = 0; u < IPWH; ++u) {
+      const int i = w + kWaves * u;
+      const int row = kRPI * i + lane / kCPR;
+      const int c = (lane % kCPR) ^ swz(row);
+      const int cm = min(m0 + row, Mc - 1);
+      const int rh = rows ? rows[cm] : cm;        // hidden row of this position
       voff_h[u] = uint32_t(rh) * uint32_t(H) * 2u + uint32_t(c) * 16u;
     }
     const bf16 *wbase = whead + int64_t(n0) * H;
@@ -192,57 +215,61 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     const uint32_t lds0 = lds_addr(ring);
     const int nk = H / kTK;
     auto issue = [&](int kt) {
-      const uint32_t st = lds0 + uint32_t((kt % kStages) * kStageBytes);
+      const uint32_t st = lds0 + uint32_t((kt % NST) * SB);
       const bf16 *wb = kPacked ? whead + (int64_t(tn) * nk + kt) * (kTN * kTK) : wbase + kt * kTK;
       const bf16 *hb = hbase + kt * kTK;
 #pragma unroll
       for (int u = 0; u < kIPW; ++u) {
         const uint32_t i = uint32_t(w + kWaves * u);
         dma16(wb, voff_w[u], __builtin_amdgcn_readfirstlane(st + i * 1024u));
+      }
+#pragma unroll
+      for (int u = 0; u < IPWH; ++u) {
+        const uint32_t i = uint32_t(w + kWaves * u);
         dma16(hb, voff_h[u], __builtin_amdgcn_readfirstlane(st + uint32_t(kTN * kRowBytes) + i * 1024u));
       }
     };
-    f32x4 acc[NI][NJ];
+    f32x4 acc[NI][NJv];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
-    for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
+      for (int j = 0; j < NJv; ++j) acc[i][j] = f32x4{};
+    for (int s = 0; s < NST - 1 && s < nk; ++s) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(kStages - 2, nk - 1 - kt);
-      wait_dma<2 * kIPW>(ahead);     // this wave's part of stage kt has landed
+      const int ahead = min(NST - 2, nk - 1 - kt);
+      wait_dma<kIPW + IPWH>(ahead);  // this wave's part of stage kt has landed
       lds_barrier();                 // all of stage kt visible; stage kt-1 free for reuse
-      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-      const unsigned char *st = ring + (kt % kStages) * kStageBytes;
+      if (kt + NST - 1 < nk) issue(kt + NST - 1);
+      const unsigned char *st = ring + (kt % NST) * SB;
       const unsigned char *wl = st, *hl = st + kTN * kRowBytes;
       // lane: row l16 of each 16-row block, hidden units ks*32 + 8*l4 .. +7
 #pragma unroll
       for (int ks = 0; ks < kTK / 32; ++ks) {
         const int c = ks * 4 + l4;
-        bf16x8 a[NI], bb[NJ];
+        bf16x8 a[NI], bb[NJv];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int row = wn * TNW + i * kMB + l16;
           a[i] = *reinterpret_cast<const bf16x8 *>(wl + row * kRowBytes + ((c ^ swz(row)) * 16));
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int row = wm * TMW + j * kMB + l16;
+        for (int j = 0; j < NJv; ++j) {
+          const int row = wm * TMWv + j * kMB + l16;
           bb[j] = *reinterpret_cast<const bf16x8 *>(hl + row * kRowBytes + ((c ^ swz(row)) * 16));
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
+          for (int j = 0; j < NJv; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
     }
     // lane: position l16 of each 16-position block, head rows 4*l4 .. +3 of
     // each 16-row block
-    float pm[NJ], pz[NJ];
-    int pi[NJ];
+    float pm[NJv], pz[NJv];
+    int pi[NJv];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < NJv; ++j) {
       float mx = kNegInf;
       int id = kNoIndex;
 #pragma unroll
@@ -268,30 +295,43 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     }
     lds_barrier();
     float *red_m = reinterpret_cast<float *>(ring);
-    float *red_z = red_m + WN * kTM;
-    int *red_i = reinterpret_cast<int *>(red_z + WN * kTM);
+    float *red_z = red_m + WN * TM;
+    int *red_i = reinterpret_cast<int *>(red_z + WN * TM);
     if (l4 == 0) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int p = wm * TMW + j * kMB + l16;
-        red_m[wn * kTM + p] = pm[j];
-        red_z[wn * kTM + p] = pz[j];
-        red_i[wn * kTM + p] = pi[j];
+      for (int j = 0; j < NJv; ++j) {
+        const int p = wm * TMWv + j * kMB + l16;
+        red_m[wn * TM + p] = pm[j];
+        red_z[wn * TM + p] = pz[j];
+        red_i[wn * TM + p] = pi[j];
       }
     }
     lds_barrier();
-    for (int p = tid; p < kTM; p += kThreads) {
+    for (int p = tid; p < TM; p += kThreads) {
       if (m0 + p >= Mc) break;
       float mx = red_m[p], z = red_z[p];
       int id = red_i[p];
 #pragma unroll
-      for (int g = 1; g < WN; ++g) merge_part(mx, z, id, red_m[g * kTM + p], red_z[g * kTM + p], red_i[g * kTM + p]);
+      for (int g = 1; g < WN; ++g) merge_part(mx, z, id, red_m[g * TM + p], red_z[g * TM + p], red_i[g * TM + p]);
       Part pt;
       pt.m = mx; pt.z = z; pt.idx = id; pt.pad = 0;
       parts[int64_t(m0 + p) * n_tiles + tn] = pt;
     }
     lds_barrier();                   // the next tile's DMA reuses the ring
   }
+}
+
+template <bool kPacked>
+__global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
+    const bf16 *__restrict__ hidden, const bf16 *__restrict__ whead, int M, int V, int H,
+    int n_tiles, const int32_t *__restrict__ rows, const int32_t *__restrict__ count,
+    Part *__restrict__ parts) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
+  const int Mc = count ? *count : M;
+  if (Mc <= kTMSmall)
+    tiles_body<kPacked, kTMSmall>(ring, hidden, whead, Mc, V, H, n_tiles, rows, parts);
+  else
+    tiles_body<kPacked, kTM>(ring, hidden, whead, Mc, V, H, n_tiles, rows, parts);
 }
 
 // One workgroup per position: the n_tiles partials, merged in tile order.

@@ -26,10 +26,11 @@
 //   - Tiles are numbered with the position tile fastest and dealt to the
 //     XCDs in contiguous ranges, so the position tiles that share a slice of
 //     the head run together on one XCD and read it from its L2.
-//   - When at most 128 positions are left (a block's late steps) the tiles
-//     are 256 x 128 with a 3-stage ring of 48 KiB stages: one position tile
-//     then streams the head, and two head stages in flight instead of one
-//     take such a call from about 258 to 192 us.
+//   - When 128-position tiles pad the positions less (at most 128 left, a
+//     block's late steps, or 257 .. 384) the tiles are 256 x 128 with a
+//     3-stage ring of 48 KiB stages: two head stages stay in flight instead
+//     of one, and no half-empty position tile is computed.  At 103 positions
+//     a call goes from about 258 to 192 us, at 266 from 457 to 421 us.
 //   Measured at 64 x 16 positions, H = 4096, V = 131072, every position
 //   scored (median of 7 x 20 launches of td_lmhead_commit): 879 us, against
 //   927 us for the same tiles on 32x32x16 blocks.  Earlier 32x32x16 layouts:
@@ -163,11 +164,9 @@ __global__ __launch_bounds__(1024) void lmhead_compact(const uint8_t *__restrict
 // workgroups in turn, so the position tiles of one head slice run at the
 // same time on one XCD and share the slice through its L2.
 //
-// TM positions per tile: 256 with a 2-stage ring of 64 KiB stages, or, when
-// at most 128 positions are left (a block's late steps), 128 with a 3-stage
-// ring of 48 KiB stages.  Then only one position tile exists and a pass over
-// the head is bound by its stream, so two stages of the head are kept in
-// flight instead of one; each wave takes 64 head rows x 32 positions.
+// TM positions per tile: 256 with a 2-stage ring of 64 KiB stages, or 128
+// with a 3-stage ring of 48 KiB stages (each wave 64 head rows x 32
+// positions), which keeps two stages of the head in flight instead of one.
 template <bool kPacked, int TM>
 __device__ __forceinline__ void tiles_body(unsigned char *ring, const bf16 *__restrict__ hidden,
                                            const bf16 *__restrict__ whead, int Mc, int V, int H,
@@ -328,7 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_tiles(
     Part *__restrict__ parts) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
   const int Mc = count ? *count : M;
-  if (Mc <= kTMSmall)
+  // 128-position tiles when they pad the positions to at most 5/6 of the
+  // rows that 256-position tiles would: per flop they run at about 0.83 of
+  // the larger tiles' rate, so they pay when they skip a padded half tile
+  // (at most 128 positions left, or 257 .. 384)
+  const int rows_s = (Mc + kTMSmall - 1) / kTMSmall * kTMSmall, rows_b = (Mc + kTM - 1) / kTM * kTM;
+  if (rows_s * 6 < rows_b * 5)
     tiles_body<kPacked, kTMSmall>(ring, hidden, whead, Mc, V, H, n_tiles, rows, parts);
   else
     tiles_body<kPacked, kTM>(ring, hidden, whead, Mc, V, H, n_tiles, rows, parts);

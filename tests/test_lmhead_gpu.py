@@ -86,6 +86,7 @@ def test_lmhead_exact_b4(gamma, frac):
     (2, 1, 64, 7),           # S = 1, tiny vocabulary
     (9, 32, 512, 2049),      # 288 rows, 9 token tiles (one token in the last)
     (16, 16, 4096, 1000),    # the widest exact hidden size
+    (24, 16, 256, 3000),     # ~288 rows: three 128-position tiles, ragged
 ])
 def test_lmhead_exact_shapes(B, S, H, V):
     w = LW["lmhead_exact_b4_h256_v5000"].with_(B=B, S=S, H=H, V=V)

@@ -59,7 +59,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGrid = 256;        // persistent: one workgroup per CU of MI355X
 constexpr int kRowBytes = kTK * 2;
 constexpr int kStageBytes = (kTN + kTM) * kRowBytes;
-constexpr int kTMSmall = 128;     // positions per tile when at most this many are left
+constexpr int kTMSmall = 128;     // positions per tile of the smaller (3-stage) tiles
 constexpr int kRingBytes = kStages * kStageBytes > 3 * (kTN + kTMSmall) * kRowBytes
                                ? kStages * kStageBytes
                                : 3 * (kTN + kTMSmall) * kRowBytes;
@@ -67,11 +67,11 @@ constexpr int kRPB = 256 / kRowBytes;          // rows per 256 bytes
 constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
 constexpr int kRPI = 1024 / kRowBytes;         // rows per 1 KiB DMA instruction
 constexpr int kInstr = kTN * kRowBytes / 1024; // DMA instructions per operand per stage
-constexpr int kIPW = kInstr / kWaves;          // per wave and operand
+constexpr int kIPW = kInstr / kWaves;          // head DMA instructions per wave and stage
 constexpr int WN = 4, WM = kWaves / 4;
-constexpr int TNW = kTN / WN, TMW = kTM / WM;
+constexpr int TNW = kTN / WN;                  // head rows per wave
 constexpr int kMB = 16;                        // v_mfma_f32_16x16x32_bf16 blocks
-constexpr int NI = TNW / kMB, NJ = TMW / kMB;
+constexpr int NI = TNW / kMB;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kNoIndex = 0x7fffffff;

@@ -35,10 +35,19 @@ int denoise(const td_attn_args *a, const td_commit_args *c, const int32_t *gate,
   rc = check_ws(wa + wc, ws, ws_bytes);
   if (rc != TD_OK) return rc;
   char *wsc = static_cast<char *>(ws) + wa;
-  if (pa.decode || !pa.mfma) {
+  if (!pa.mfma) {
     rc = attn_launch(a, pa, ws, stream, gate);
     if (rc != TD_OK) return rc;
     return launch_commit(c, pc, wsc, stream, gate);
+  }
+  if (pa.decode) {
+    // decode path: the streaming kernel, the commit's row pass, then one
+    // launch for the decode merge and the commit decision
+    rc = launch_attn_decode(a, pa, ws, stream, gate, false);
+    if (rc != TD_OK) return rc;
+    rc = launch_commit(c, pc, wsc, stream, gate, false);
+    if (rc != TD_OK) return rc;
+    return launch_decode_step_tail(a, pa, ws, c, pc, wsc, stream, gate);
   }
   // MFMA path: attention main kernel, the commit's row pass, then one launch
   // for both small tails (attention merge + commit decision)

@@ -31,6 +31,7 @@
 //   unit merges its pieces (deterministic order) and writes out.
 #include <hip/hip_runtime.h>
 
+#include "td_finalize.h"
 #include "td_internal.h"
 
 namespace td {
@@ -355,12 +356,10 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void attn_decode(
 // share online with all its loads in flight at once, and the 8 group
 // results are merged in group order through LDS (deterministic).  Units a
 // single wave covered were written by it.
-__global__ __launch_bounds__(256) void decode_merge(
-    int B, int S, int Hq, int Hkv, int G, const int64_t *__restrict__ pre, int NW,
-    const bf16 *__restrict__ ws_o, const float2 *__restrict__ ws_ml, bf16 *__restrict__ out,
-    const int32_t *__restrict__ gate) {
-  if (gate && *gate == 0) return;
-  const int n = blockIdx.x & 15, unit = blockIdx.x >> 4;
+__device__ __forceinline__ void decode_merge_block(
+    unsigned blk, int B, int S, int Hq, int Hkv, int G, const int64_t *__restrict__ pre, int NW,
+    const bf16 *__restrict__ ws_o, const float2 *__restrict__ ws_ml, bf16 *__restrict__ out) {
+  const int n = blk & 15, unit = blk >> 4;
   const int M = G * S;
   if (n >= M) return;                           // uniform per workgroup: no barrier is skipped
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
@@ -434,10 +433,42 @@ __global__ __launch_bounds__(256) void decode_merge(
       make_uint2(pack_bf16(A[0] * inv, A[1] * inv), pack_bf16(A[2] * inv, A[3] * inv));
 }
 
+__global__ __launch_bounds__(256) void decode_merge(
+    int B, int S, int Hq, int Hkv, int G, const int64_t *__restrict__ pre, int NW,
+    const bf16 *__restrict__ ws_o, const float2 *__restrict__ ws_ml, bf16 *__restrict__ out,
+    const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
+  decode_merge_block(blockIdx.x, B, S, Hq, Hkv, G, pre, NW, ws_o, ws_ml, out);
+}
+
+// The tail of a denoise step on the decode path in one launch: the merge of
+// the cut units (blocks [0, merge_blocks), as decode_merge) and, beside it,
+// the commit's block decision (the remaining blocks, one wave per sequence,
+// as commit_finalize).  The two share no data; one launch instead of two
+// saves a launch and its drain.
+__global__ __launch_bounds__(256) void decode_step_tail(
+    int B, int S, int Hq, int Hkv, int G, const int64_t *__restrict__ pre, int NW,
+    const bf16 *__restrict__ ws_o, const float2 *__restrict__ ws_ml, bf16 *__restrict__ out,
+    unsigned merge_blocks, const Part *__restrict__ parts, int R, float gamma,
+    const uint8_t *masked_in, uint8_t *__restrict__ commit, int32_t *__restrict__ token,
+    float *__restrict__ maxprob, int32_t *__restrict__ n_commit, uint8_t *masked_out,
+    int32_t *__restrict__ tokens, int32_t *__restrict__ n_masked_left,
+    const int32_t *__restrict__ gate) {
+  if (gate && *gate == 0) return;
+  if (blockIdx.x < merge_blocks) {
+    decode_merge_block(blockIdx.x, B, S, Hq, Hkv, G, pre, NW, ws_o, ws_ml, out);
+    return;
+  }
+  const int b = int(blockIdx.x - merge_blocks) * 4 + int(threadIdx.x >> 6);
+  if (b < B)
+    fin::finalize_seq(b, threadIdx.x & 63, parts, S, R, gamma, masked_in, commit, token, maxprob,
+                      n_commit, masked_out, tokens, n_masked_left, false);
+}
+
 }  // namespace
 
 int launch_attn_decode(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
-                       const int32_t *gate) {
+                       const int32_t *gate, bool merge) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char *w = static_cast<char *>(ws);
   int64_t *pre = reinterpret_cast<int64_t *>(w + p.off_prefix);
@@ -451,8 +482,26 @@ int launch_attn_decode(const td_attn_args *a, const AttnPlan &p, void *ws, void 
                      static_cast<const bf16 *>(a->v_ctx), a->ctx_offsets, a->total_ctx, max_ctx,
                      a->B, a->S, a->Hq, a->Hkv, p.G, p.scale_log2, pre, nw, o, ml,
                      static_cast<bf16 *>(a->out), gate);
-  hipLaunchKernelGGL(decode_merge, dim3(unsigned(a->B * a->Hkv * 16)), dim3(256), 0, st, a->B,
-                     a->S, a->Hq, a->Hkv, p.G, pre, nw, o, ml, static_cast<bf16 *>(a->out), gate);
+  if (merge)
+    hipLaunchKernelGGL(decode_merge, dim3(unsigned(a->B * a->Hkv * 16)), dim3(256), 0, st, a->B,
+                       a->S, a->Hq, a->Hkv, p.G, pre, nw, o, ml, static_cast<bf16 *>(a->out), gate);
+  return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
+}
+
+int launch_decode_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws,
+                            const td_commit_args *c, const CommitPlan &pc, void *ws_commit,
+                            void *stream, const int32_t *gate) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char *w = static_cast<char *>(ws);
+  const unsigned merge_blocks = unsigned(a->B * a->Hkv * 16);
+  const unsigned fin_blocks = unsigned((c->B + 3) / 4);
+  hipLaunchKernelGGL(decode_step_tail, dim3(merge_blocks + fin_blocks), dim3(256), 0, st, a->B, a->S,
+                     a->Hq, a->Hkv, p.G, reinterpret_cast<const int64_t *>(w + p.off_prefix),
+                     p.launch * kDecWaves, reinterpret_cast<const bf16 *>(w + p.off_o),
+                     reinterpret_cast<const float2 *>(w + p.off_ml), static_cast<bf16 *>(a->out),
+                     merge_blocks, static_cast<const Part *>(ws_commit), pc.R, c->gamma,
+                     c->masked_in, c->commit, c->token, c->maxprob, c->n_commit, c->masked_out,
+                     c->tokens, c->n_masked_left, gate);
   return hipGetLastError() == hipSuccess ? TD_OK : TD_ERR_HIP;
 }
 

@@ -74,8 +74,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // launch_step_tail
 int launch_attn(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
                 const int32_t *gate = nullptr, bool merge = true);
+// merge = false: the streaming kernel alone; the merge then runs in
+// launch_decode_step_tail
 int launch_attn_decode(const td_attn_args *a, const AttnPlan &p, void *ws, void *stream,
-                       const int32_t *gate = nullptr);
+                       const int32_t *gate = nullptr, bool merge = true);
 // finalize = false: the row pass alone; the decision then runs in launch_step_tail
 int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *stream,
                   const int32_t *gate = nullptr, bool finalize = true);
@@ -84,6 +86,11 @@ int launch_commit(const td_commit_args *c, const CommitPlan &p, void *ws, void *
 // attention's workspace, ws_commit the commit's
 int launch_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws, const td_commit_args *c,
                      const CommitPlan &pc, void *ws_commit, void *stream, const int32_t *gate);
+// the same on the decode attention path: the decode merge and the commit's
+// decision in one launch (td_decode.hip)
+int launch_decode_step_tail(const td_attn_args *a, const AttnPlan &p, void *ws,
+                            const td_commit_args *c, const CommitPlan &pc, void *ws_commit,
+                            void *stream, const int32_t *gate);
 int launch_append(const td_append_args *p, void *stream);
 // the commit's per-sequence decision over R parts per position (td_commit.hip)
 int launch_commit_finalize(const Part *parts, int R, int B, int S, float gamma,

@@ -321,13 +321,21 @@ def _run_step(w, da, dc, a, gamma):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32_b1_ctx64", "bf16_b8_ctx4k", "bf16_b64_ragged1k_8k"])
+def _decode_step_workload():
+    # G*S = 16 with S = 4: the decode attention path with several positions
+    return W["bf16_b8_ctx4k"].with_(B=5, S=4, Hq=8, Hkv=2, V=5000)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_b1_ctx64", "bf16_b8_ctx4k", "bf16_b64_ragged1k_8k",
+                                  "bf16_b64_ragged1k_8k_s1", "decode_b5_s4"])
 def test_denoise_step(name):
-    """td_denoise_step (on the MFMA path: attention main kernel, commit row
-    pass, then the tail launch that merges the attention and takes the
-    commit decision) against oracle.denoise_step, every sequence and every
-    position, including the headline batch."""
-    w = W[name]
+    """td_denoise_step against oracle.denoise_step, every sequence and every
+    position, including the headline batch.  On the MFMA path: attention main
+    kernel, commit row pass, then the tail launch that merges the attention
+    and takes the commit decision; at S = 1 (and G*S <= 16) the decode path:
+    the streaming kernel, the row pass, then one launch for the decode merge
+    and the decision."""
+    w = _decode_step_workload() if name == "decode_b5_s4" else W[name]
     a, c, el, da, dc = _step_inputs(w, 3001, 0.8)
     log("case denoise step", name)
     _run_step(w, da, dc, a, w.gamma)

@@ -28,7 +28,9 @@
 //     inside one wave's run is normalised and written out; a cut unit's
 //     pieces write (m, l) in fp32 and O / l in bf16 to the workspace.
 // decode_merge: one workgroup per (sequence, KV head, query row) of a cut
-//   unit merges its pieces (deterministic order) and writes out.
+//   unit merges its pieces (deterministic order) and writes out.  In a
+//   denoise step the same blocks run inside decode_step_tail, beside the
+//   commit's per-sequence decision.
 #include <hip/hip_runtime.h>
 
 #include "td_finalize.h"
